@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the per-matrix Muon update.
+
+A step is one muon_step over the workload's whole matrix list (momentum, normalisation,
+Newton-Schulz in the dispatcher's form per shape, fused weight update), inputs resident
+in HBM. Prints one JSON line:
+  value / ms_per_step  event-timed optimizer-step latency (lower is better)
+  roofline             the dominant kernel's algorithmic FLOP rate against the bf16 dense
+                       MFMA peak, from per-launch hipEvents recorded by the library on the
+                       launch stream during a second timed pass
+  cpu_baseline         the fp64 oracle on the host cores, on a bounded sample
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "f32": 157.3}       # dense MFMA TFLOP/s (MI355X public figures)
+HBM_PEAK_GBS = 8000.0
+GEMM_STAGES = ("syrk", "square", "apply", "apply_update")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="single_bf16_2560x9728")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=30.0)
+    ap.add_argument("--details", action="store_true", help="also print the per-stage table to stderr")
+    return ap.parse_args()
+
+
+def make_inputs(w, torch):
+    from matrix_orthogonalising_optimizer_muon_amd import workloads as wl
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    host = w.elements <= 64 * 1024 * 1024
+    Ws, Gs, Ms = [], [], []
+    for i, spec in enumerate(w.matrices):
+        if host:
+            Ws.append(torch.from_numpy(wl.weight_np(w, i)).to("cuda").to(tdt[w.w_dtype]))
+            Gs.append(torch.from_numpy(wl.gradient_np(w, 0, i)).to("cuda").to(tdt[w.g_dtype]))
+        else:
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(1000 + i)
+            Ws.append((0.02 * torch.randn(spec.rows, spec.cols, generator=gen, device="cuda")).to(tdt[w.w_dtype]))
+            Gs.append(wl.gradient_torch(w, 0, i, "cuda"))
+        Ms.append(torch.zeros(spec.rows, spec.cols, dtype=tdt[w.m_dtype], device="cuda"))
+    return Ws, Gs, Ms, ("seeded numpy draw" if host else "seeded torch device draw")
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands, timed on the host: whole matrices in list order until the
+    time budget is spent, scaled to the full workload by the sampled share of the
+    dispatcher-model FLOPs (exact when the whole list fits)."""
+    from matrix_orthogonalising_optimizer_muon_amd import workloads as wl
+    from oracle import flop_model
+    from oracle import muon as om
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+
+    def mode_of(s):
+        g = flop_model.dense_flops(s.rows, s.cols, "gram")
+        p = flop_model.dense_flops(s.rows, s.cols, "plain")
+        return "gram" if g < p else "plain"
+
+    total_flops = sum(flop_model.dense_flops(s.rows, s.cols, mode_of(s)) for s in w.matrices)
+    done_flops, t_used, n_done = 0.0, 0.0, 0
+    for i, s in enumerate(w.matrices):
+        W = wl.weight_np(w, i).astype(np.float64)
+        G = wl.gradient_np(w, 0, i).astype(np.float64)
+        M = np.zeros_like(G)
+        t0 = time.perf_counter()
+        om.muon_step(W, G, M, lr=w.lr, mu=w.mu, wd=w.wd, mode=mode_of(s))
+        t_used += time.perf_counter() - t0
+        done_flops += flop_model.dense_flops(s.rows, s.cols, mode_of(s))
+        n_done += 1
+        if t_used >= budget_s:
+            break
+    scale = total_flops / done_flops
+    sample = (f"{n_done} of {len(w.matrices)} matrices, one full oracle step each (fp64 NumPy, "
+              f"{t_used:.1f} s)" + ("" if n_done == len(w.matrices) else
+                                    f"; scaled x{scale:.2f} by model FLOPs to the whole list"))
+    return {"value": round(t_used * scale * 1e3, 3), "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": sample}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "exchange of the update is not built here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from matrix_orthogonalising_optimizer_muon_amd import binding as B
+    from matrix_orthogonalising_optimizer_muon_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    print(f"[bench] workload {w.name}: {len(w.matrices)} matrices, {w.elements / 1e6:.1f} M elements",
+          file=sys.stderr, flush=True)
+    Ws, Gs, Ms, data = make_inputs(w, torch)
+    mats = list(zip(Ws, Gs, Ms))
+    hp = B.make_hparams(lr=w.lr, momentum=w.mu, weight_decay=w.wd, mode="auto",
+                        w_dtype=w.w_dtype, g_dtype=w.g_dtype, m_dtype=w.m_dtype, ns_dtype=w.ns_dtype)
+    ctx = B.muon_init(0)
+    pctx = B.muon_init(0, B.MUON_FLAG_PROFILE)
+    arr = B.matrix_list(mats)
+    nbytes = B.muon_workspace_size(ctx, mats, hp)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(c):
+        B.check(B.muon_step(c, arr, hp, ws.data_ptr(), nbytes, sp, count=len(mats)), "muon_step")
+
+    for _ in range(args.warmup):
+        step(ctx)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps), workspace {nbytes / 2**30:.2f} GiB",
+          file=sys.stderr, flush=True)
+
+    # Timed region: exactly K steps between two events on the launch stream.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step(ctx)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
+          file=sys.stderr, flush=True)
+
+    # Second pass with per-launch events (library profiler) for the per-kernel roofline.
+    for _ in range(args.steps):
+        step(pctx)
+    torch.cuda.synchronize()
+    prof = B.muon_profile_read(pctx, 4096)
+    gemm = [e for e in prof if e["stage"] in GEMM_STAGES]
+    dom = max(gemm, key=lambda e: e["total_ms"])
+    avg_ms = dom["total_ms"] / dom["launches"]
+    per_launch_flops = dom["flops"] / dom["launches"]
+    achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK[w.ns_dtype]
+    gemm_flops = sum(e["flops"] for e in gemm) / args.steps
+    gemm_ms = sum(e["total_ms"] for e in gemm) / args.steps
+    mom = [e for e in prof if e["stage"] == "momentum"]
+    mom_gbs = (sum(e["bytes"] for e in mom) / (sum(e["total_ms"] for e in mom) * 1e-3) / 1e9) if mom else None
+    prof_ms = sum(e["total_ms"] for e in prof) / args.steps
+    if args.details:
+        for e in prof:
+            rate = (e["flops"] / (e["total_ms"] * 1e-3) / 1e12) if e["flops"] else 0.0
+            print(f"[stage] {e['stage']:14s} m'={e['m']:6d} n'={e['n']:6d} x{e['count']:4d} "
+                  f"launches={e['launches']:5d} avg={e['total_ms'] / e['launches'] * 1e3:9.2f} us "
+                  f"{rate:8.1f} TFLOP/s", file=sys.stderr)
+
+    out = {
+        "metric": "Muon optimizer-step ms per shape set; GEMM TFLOP/s as % of bf16 MFMA peak",
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.ns_dtype == "bf16" else "f32",
+        "data": f"synthetic ({data})",
+        "config": {"workload": w.name, "matrices": len(w.matrices), "elements": w.elements,
+                   "shapes": sorted({f"{s.rows}x{s.cols}" for s in w.matrices}),
+                   "ns": "auto (FLOP-model dispatch: Gram 2+2+1 or plain 5 rounds)",
+                   "storage": {"W": w.w_dtype, "G": w.g_dtype, "M": w.m_dtype}},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": f"{dom['stage']} m'={dom['m']} n'={dom['n']} x{dom['count']}",
+                     "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "flops_per_launch": per_launch_flops},
+        "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "gemm_frac_of_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak, 4),
+        "momentum_gbs": None if mom_gbs is None else round(mom_gbs, 1),
+        "momentum_frac_of_hbm": None if mom_gbs is None else round(mom_gbs / HBM_PEAK_GBS, 4),
+        "profiled_ms_per_step": round(prof_ms, 4),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    B.muon_destroy(ctx)
+    B.muon_destroy(pctx)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * muon.h - C ABI of the MI355X (gfx950) per-matrix Muon update library (libmuon_amd.so).
+ *
+ * What one call computes, per matrix (see the citations at each entry point):
+ *   M' = mu*M + G;  U = G + mu*M' (Nesterov) or U = M'
+ *   X0 = U / (||U||_F + eps), on the short side (tall matrices are handled as U^T)
+ *   quintic Newton-Schulz with coefficients (a, b, c): plain rounds, or the Gram-space
+ *   form with segments (default 2+2+1)
+ *   W' = W*(1 - lr*wd) - lr*O, with O the NS result in W's orientation
+ *
+ * Sources: "MuonX" article (Baidu Baige, damodev.csdn.net), sections 2 and 3.2 (Gram NS);
+ * "DMuon: Efficient Distributed Muon Training with Near-Adam Overhead" (gist.science
+ * summary), technical summary sections 2.2 (Gram NS, symmetric SYRK Gram product,
+ * batching of similar shapes) and 2.4 (shape-adaptive kernel choice, cached).
+ *
+ * Conventions for every entry point:
+ *   - every function returns an int status (MUON_OK or a negative MUON_ERR_*) and never
+ *     throws, aborts or exits;
+ *   - every argument is validated on the host before anything is enqueued: on any error
+ *     nothing has been launched and W, M are untouched;
+ *   - device pointers are plain device addresses on the context's device; host pointers
+ *     are read during the call only;
+ *   - the library allocates no device memory: scratch space is the caller's workspace.
+ */
+#ifndef MUON_AMD_H
+#define MUON_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define MUON_OK 0
+#define MUON_ERR_ARG -1          /* null pointer, bad size, bad hyper-parameter, bad dtype */
+#define MUON_ERR_WORKSPACE -2    /* workspace null, too small or misaligned (needs 256 B) */
+#define MUON_ERR_DEVICE -3       /* device index invalid or not a gfx950 GPU */
+#define MUON_ERR_HIP -4          /* a HIP runtime call or kernel launch failed */
+#define MUON_ERR_UNSUPPORTED -5  /* valid request the library does not implement */
+
+/* ---- storage dtypes ---- */
+#define MUON_F32 0
+#define MUON_BF16 1
+
+/* ---- Newton-Schulz form ---- */
+#define MUON_NS_AUTO 0   /* per shape: the dispatcher picks plain or Gram */
+#define MUON_NS_PLAIN 1  /* sum(segments) plain rounds (segments ignored otherwise) */
+#define MUON_NS_GRAM 2   /* Gram-space NS with the given segments */
+
+#define MUON_MAX_SEGMENTS 8
+
+/* ---- muon_init flags ---- */
+#define MUON_FLAG_MODEL_ONLY 1u  /* dispatcher uses the FLOP model only (no timed tuning) */
+#define MUON_FLAG_PROFILE 2u     /* bracket every launch with hipEvents (muon_profile_read) */
+
+typedef struct muon_ctx muon_ctx; /* opaque; owned by the library */
+
+/* One 2-D weight. All three arrays are rows x cols, row-major, leading dimension cols,
+ * on the context's device, in the dtypes named by muon_hparams. W and M are updated in
+ * place; G is read only. Arrays of different matrices must not overlap. */
+typedef struct muon_matrix {
+  void *W;
+  const void *G;
+  void *M;
+  int64_t rows;
+  int64_t cols;
+} muon_matrix;
+
+/* Hyper-parameters of one call (shared by every matrix of the call).
+ *   lr, weight_decay:   W' = W*(1 - lr*weight_decay) - lr*O   (lr > 0 not required)
+ *   momentum (mu):      0 <= mu < 1
+ *   eps:                >= 0, added to the Frobenius norm
+ *   nesterov:           0 or 1
+ *   a, b, c:            quintic NS coefficients (finite)
+ *   n_segments, segments[]: 1..MUON_MAX_SEGMENTS segments, each >= 1; their sum is the
+ *                       number of NS rounds (at most 64)
+ *   mode:               MUON_NS_AUTO | MUON_NS_PLAIN | MUON_NS_GRAM
+ *   w_dtype:            MUON_F32 or MUON_BF16
+ *   g_dtype, m_dtype:   MUON_F32 or MUON_BF16
+ *   ns_dtype:           MUON_BF16: bf16 iterate with fp32-accumulate MFMA, the m'xm'
+ *                       recurrence in fp16 (prescaled); MUON_F32: fp32 throughout        */
+typedef struct muon_hparams {
+  float lr;
+  float momentum;
+  float weight_decay;
+  float eps;
+  int32_t nesterov;
+  float a, b, c;
+  int32_t n_segments;
+  int32_t segments[MUON_MAX_SEGMENTS];
+  int32_t mode;
+  int32_t w_dtype;
+  int32_t g_dtype;
+  int32_t m_dtype;
+  int32_t ns_dtype;
+} muon_hparams;
+
+/* Per-matrix plan as chosen by the dispatcher (muon_plan_info). */
+typedef struct muon_plan_entry {
+  int32_t mode;          /* MUON_NS_PLAIN or MUON_NS_GRAM actually used */
+  int32_t transposed;    /* 1 if rows > cols (processed as the transpose) */
+  int64_t m, n;          /* canonical short side m' and long side n' */
+  int32_t group;         /* same-shape group index (one batched launch per stage) */
+  int32_t tile;          /* tile edge of the GEMM kernels used (64 or 128) */
+  double dense_flops;    /* matmul FLOPs as the MuonX article counts them (2m'^2n', 2m'^3) */
+  double kernel_flops;   /* FLOPs the kernels actually perform (symmetric outputs halved) */
+} muon_plan_entry;
+
+/* Aggregated launch timings of one stage kind and shape (muon_profile_read). */
+typedef struct muon_profile_entry {
+  char stage[32];        /* "table", "momentum", "norm_finalize", "syrk", "square",
+                            "apply", "apply_update" */
+  int64_t m, n;          /* canonical shape of the group the launches served */
+  int32_t count;         /* matrices per launch */
+  int32_t launches;      /* launches aggregated */
+  double total_ms;       /* sum of event-measured launch durations */
+  double flops;          /* algorithmic FLOPs of those launches (one triangle for
+                            symmetric outputs) */
+  double bytes;          /* algorithmic HBM bytes (elementwise stages, W in the update) */
+} muon_profile_entry;
+
+/* Defaults: lr 0.02, momentum 0.95 Nesterov, wd 0, eps 1e-7, (a, b, c) =
+ * (3.4445, -4.7750, 2.0315), segments 2+2+1, mode AUTO, W fp32, G and M bf16, NS bf16. */
+void muon_hparams_default(muon_hparams *hp);
+
+/* Create a context on HIP device `device`. The device must be gfx950, else
+ * MUON_ERR_DEVICE. device == -1 creates a host-only context (no HIP call is made; it
+ * plans for a 256-CU MI355X): muon_workspace_size and muon_plan_info work, muon_step and
+ * muon_debug_gemm validate their arguments and then return MUON_ERR_DEVICE.
+ * `flags` is 0 or a combination of MUON_FLAG_MODEL_ONLY and MUON_FLAG_PROFILE. *out receives the context; it is owned by the
+ * caller until muon_destroy. No device memory is allocated. */
+int muon_init(muon_ctx **out, int device, uint32_t flags);
+
+/* Bytes of device workspace muon_step needs for this list and these hyper-parameters
+ * (deterministic for a given list of shapes and hparams). Same validation as muon_step
+ * except that array pointers may be null. */
+int muon_workspace_size(muon_ctx *ctx, const muon_matrix *mats, int count,
+                        const muon_hparams *hp, size_t *bytes);
+
+/* One Muon update of `count` matrices (count == 0 is a no-op), enqueued on `stream`
+ * (a hipStream_t; null = the default stream). Asynchronous: returns after enqueueing,
+ * with no host synchronisation; W, G, M and the workspace must stay valid until the
+ * stream work completes. `workspace` is device memory of at least muon_workspace_size
+ * bytes, 256-byte aligned, owned by the caller and not used by anything else until the
+ * step completes. Each matrix's result equals a separate call for it (grouping only
+ * batches launches). Launch failures return MUON_ERR_HIP; device faults surface at the
+ * caller's next synchronisation. A context must not be used by two threads at once. */
+int muon_step(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hparams *hp,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Plan of matrix `index` of the list (host-only; nothing is launched). */
+int muon_plan_info(muon_ctx *ctx, const muon_matrix *mats, int count,
+                   const muon_hparams *hp, int index, muon_plan_entry *out);
+
+/* Test-only entry point: one GEMM stage of the pipeline on caller buffers, synchronously
+ * enqueued on `stream`. kind: 0 = symmetric X X^T (bf16 in, fp16 out; or fp32), upper
+ * tiles mirrored; 1 = symmetric-output square product A B^T with epilogue
+ * alpha*acc + beta*E + gamma*I (fp16 or fp32); 2 = apply C = alpha*A*(bscale*B) + beta*E
+ * with B (K x N row-major, bf16 converted to fp16, or fp32) and C in B's dtype.
+ * ns_dtype selects the bf16/fp16 or the fp32 kernels; tile is 64 or 128. Buffers are
+ * dense row-major with leading dimension equal to their column count; M, N, K must be
+ * multiples of 64. */
+int muon_debug_gemm(muon_ctx *ctx, int kind, int ns_dtype, int tile, int64_t M, int64_t N,
+                    int64_t K, const void *A, const void *B, const void *E, void *C,
+                    float alpha, float beta, float gamma, float bscale, void *stream);
+
+/* Profiler read-out for a context created with MUON_FLAG_PROFILE: waits for the last
+ * recorded launch, aggregates all launches recorded since the previous read by (stage,
+ * shape, batch) in first-seen order into out[0..capacity), stores the number of entries
+ * in *n_out and clears the record. Returns MUON_ERR_ARG when the context was created
+ * without the flag or when more than `capacity` entries exist (then *n_out tells how
+ * many are needed and the record is cleared). */
+int muon_profile_read(muon_ctx *ctx, muon_profile_entry *out, int capacity, int *n_out);
+
+/* Release a context (null is accepted). Work already enqueued is not affected. */
+int muon_destroy(muon_ctx *ctx);
+
+/* Static, human-readable text for a status code. */
+const char *muon_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_AMD_H */

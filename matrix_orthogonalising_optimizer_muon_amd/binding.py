@@ -1,0 +1,232 @@
+"""ctypes binding of ``libmuon_amd.so`` (the C ABI declared in ``include/muon.h``).
+
+Argument marshalling only: the functions carry the C names and hand plain pointers,
+sizes and structs to the library, where every step of the update runs in HIP kernels.
+There is no fallback: if the library is missing this module raises on import.
+
+torch is imported first so that the library binds to the HIP runtime torch already
+loaded (same SONAME); device buffers and streams then come from torch tensors and
+``torch.cuda.Stream`` objects.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the process's HIP runtime before the library)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("MUON_AMD_LIB", os.path.join(_HERE, "libmuon_amd.so"))
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libmuon_amd.so not found at {LIB_PATH}: build it first "
+        "(python -m matrix_orthogonalising_optimizer_muon_amd.build)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---- constants (mirror include/muon.h) ----
+MUON_OK = 0
+MUON_ERR_ARG = -1
+MUON_ERR_WORKSPACE = -2
+MUON_ERR_DEVICE = -3
+MUON_ERR_HIP = -4
+MUON_ERR_UNSUPPORTED = -5
+MUON_F32 = 0
+MUON_BF16 = 1
+MUON_NS_AUTO = 0
+MUON_NS_PLAIN = 1
+MUON_NS_GRAM = 2
+MUON_MAX_SEGMENTS = 8
+MUON_FLAG_MODEL_ONLY = 1
+MUON_FLAG_PROFILE = 2
+
+DTYPES = {"f32": MUON_F32, "bf16": MUON_BF16}
+MODES = {"auto": MUON_NS_AUTO, "plain": MUON_NS_PLAIN, "gram": MUON_NS_GRAM}
+
+
+class muon_matrix(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("G", ctypes.c_void_p), ("M", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class muon_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("eps", ctypes.c_float),
+                ("nesterov", ctypes.c_int32), ("a", ctypes.c_float), ("b", ctypes.c_float),
+                ("c", ctypes.c_float), ("n_segments", ctypes.c_int32),
+                ("segments", ctypes.c_int32 * MUON_MAX_SEGMENTS), ("mode", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("g_dtype", ctypes.c_int32),
+                ("m_dtype", ctypes.c_int32), ("ns_dtype", ctypes.c_int32)]
+
+
+class muon_plan_entry(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("transposed", ctypes.c_int32),
+                ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("group", ctypes.c_int32),
+                ("tile", ctypes.c_int32), ("dense_flops", ctypes.c_double),
+                ("kernel_flops", ctypes.c_double)]
+
+
+class muon_profile_entry(ctypes.Structure):
+    _fields_ = [("stage", ctypes.c_char * 32), ("m", ctypes.c_int64), ("n", ctypes.c_int64),
+                ("count", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_lib.muon_hparams_default.argtypes = [ctypes.POINTER(muon_hparams)]
+_lib.muon_hparams_default.restype = None
+_lib.muon_init.argtypes = [ctypes.POINTER(_P), ctypes.c_int, ctypes.c_uint32]
+_lib.muon_init.restype = ctypes.c_int
+_lib.muon_workspace_size.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int,
+                                     ctypes.POINTER(muon_hparams), ctypes.POINTER(ctypes.c_size_t)]
+_lib.muon_workspace_size.restype = ctypes.c_int
+_lib.muon_step.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int,
+                           ctypes.POINTER(muon_hparams), _P, ctypes.c_size_t, _P]
+_lib.muon_step.restype = ctypes.c_int
+_lib.muon_plan_info.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int,
+                                ctypes.POINTER(muon_hparams), ctypes.c_int,
+                                ctypes.POINTER(muon_plan_entry)]
+_lib.muon_plan_info.restype = ctypes.c_int
+_lib.muon_debug_gemm.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, ctypes.c_float,
+                                 ctypes.c_float, ctypes.c_float, ctypes.c_float, _P]
+_lib.muon_debug_gemm.restype = ctypes.c_int
+_lib.muon_profile_read.argtypes = [_P, ctypes.POINTER(muon_profile_entry), ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_int)]
+_lib.muon_profile_read.restype = ctypes.c_int
+_lib.muon_destroy.argtypes = [_P]
+_lib.muon_destroy.restype = ctypes.c_int
+_lib.muon_status_str.argtypes = [ctypes.c_int]
+_lib.muon_status_str.restype = ctypes.c_char_p
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {muon_status_str(status)}")
+        self.status = status
+
+
+def check(status: int, where: str = "muon") -> None:
+    if status != MUON_OK:
+        raise MuonError(status, where)
+
+
+def muon_status_str(status: int) -> str:
+    return _lib.muon_status_str(int(status)).decode()
+
+
+def muon_hparams_default() -> muon_hparams:
+    hp = muon_hparams()
+    _lib.muon_hparams_default(ctypes.byref(hp))
+    return hp
+
+
+def make_hparams(*, lr=None, momentum=None, weight_decay=None, eps=None, nesterov=None,
+                 coeffs=None, segments=None, mode=None, w_dtype=None, g_dtype=None,
+                 m_dtype=None, ns_dtype=None) -> muon_hparams:
+    """Defaults from the library, with the given fields replaced (names as in muon.h)."""
+    hp = muon_hparams_default()
+    if lr is not None: hp.lr = lr
+    if momentum is not None: hp.momentum = momentum
+    if weight_decay is not None: hp.weight_decay = weight_decay
+    if eps is not None: hp.eps = eps
+    if nesterov is not None: hp.nesterov = int(nesterov)
+    if coeffs is not None: hp.a, hp.b, hp.c = coeffs
+    if segments is not None:
+        segs = list(segments)
+        hp.n_segments = len(segs)
+        for i in range(MUON_MAX_SEGMENTS):
+            hp.segments[i] = segs[i] if i < len(segs) else 0
+    if mode is not None: hp.mode = MODES.get(mode, mode)
+    if w_dtype is not None: hp.w_dtype = DTYPES.get(w_dtype, w_dtype)
+    if g_dtype is not None: hp.g_dtype = DTYPES.get(g_dtype, g_dtype)
+    if m_dtype is not None: hp.m_dtype = DTYPES.get(m_dtype, m_dtype)
+    if ns_dtype is not None: hp.ns_dtype = DTYPES.get(ns_dtype, ns_dtype)
+    return hp
+
+
+def matrix_list(mats) -> ctypes.Array:
+    """Build a ``muon_matrix[]`` from (W, G, M) torch tensors or (W, G, M, rows, cols)
+    tuples of raw pointers."""
+    arr = (muon_matrix * max(1, len(mats)))()
+    for i, t in enumerate(mats):
+        if len(t) == 3:
+            W, G, M = t
+            for x in (W, G, M):
+                if x.dim() != 2 or not x.is_contiguous():
+                    raise ValueError("W, G, M must be contiguous 2-D tensors")
+            if not (W.shape == G.shape == M.shape):
+                raise ValueError("W, G, M shapes differ")
+            arr[i] = muon_matrix(W.data_ptr(), G.data_ptr(), M.data_ptr(), W.shape[0], W.shape[1])
+        else:
+            W, G, M, r, c = t
+            arr[i] = muon_matrix(W, G, M, r, c)
+    return arr
+
+
+def muon_init(device: int = 0, flags: int = 0) -> ctypes.c_void_p:
+    ctx = ctypes.c_void_p()
+    check(_lib.muon_init(ctypes.byref(ctx), int(device), int(flags)), "muon_init")
+    return ctx
+
+
+def muon_workspace_size(ctx, mats, hp: muon_hparams) -> int:
+    arr = mats if isinstance(mats, ctypes.Array) else matrix_list(mats)
+    n = len(mats)
+    out = ctypes.c_size_t()
+    check(_lib.muon_workspace_size(ctx, arr, n, ctypes.byref(hp), ctypes.byref(out)),
+          "muon_workspace_size")
+    return int(out.value)
+
+
+def muon_step(ctx, mats, hp: muon_hparams, workspace_ptr: int, workspace_bytes: int,
+              stream_ptr: int | None = None, count: int | None = None) -> int:
+    """Enqueue one update; returns the status (use ``check`` to raise)."""
+    arr = mats if isinstance(mats, ctypes.Array) else matrix_list(mats)
+    n = len(mats) if count is None else count
+    if stream_ptr is None:
+        stream_ptr = torch.cuda.current_stream().cuda_stream
+    return _lib.muon_step(ctx, arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace_ptr),
+                          ctypes.c_size_t(workspace_bytes), ctypes.c_void_p(stream_ptr))
+
+
+def muon_plan_info(ctx, mats, hp: muon_hparams, index: int) -> muon_plan_entry:
+    arr = mats if isinstance(mats, ctypes.Array) else matrix_list(mats)
+    out = muon_plan_entry()
+    check(_lib.muon_plan_info(ctx, arr, len(mats), ctypes.byref(hp), int(index), ctypes.byref(out)),
+          "muon_plan_info")
+    return out
+
+
+def muon_debug_gemm(ctx, kind, ns_dtype, tile, M, N, K, A, B, E, C, alpha=1.0, beta=0.0,
+                    gamma=0.0, bscale=1.0, stream_ptr=None) -> int:
+    if stream_ptr is None:
+        stream_ptr = torch.cuda.current_stream().cuda_stream
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    return _lib.muon_debug_gemm(ctx, int(kind), DTYPES.get(ns_dtype, ns_dtype), int(tile), M, N, K,
+                                ptr(A), ptr(B), ptr(E), ptr(C), alpha, beta, gamma, bscale,
+                                ctypes.c_void_p(stream_ptr))
+
+
+def muon_profile_read(ctx, capacity: int = 256) -> list:
+    """Aggregated per-stage launch timings since the last read, as dicts."""
+    buf = (muon_profile_entry * capacity)()
+    n = ctypes.c_int()
+    check(_lib.muon_profile_read(ctx, buf, capacity, ctypes.byref(n)), "muon_profile_read")
+    return [dict(stage=e.stage.decode(), m=e.m, n=e.n, count=e.count, launches=e.launches,
+                 total_ms=e.total_ms, flops=e.flops, bytes=e.bytes) for e in buf[:n.value]]
+
+
+def muon_destroy(ctx) -> int:
+    return _lib.muon_destroy(ctx)
+
+
+def exported_symbols() -> list:
+    """Names of the C entry points this binding resolved (each must exist in the .so)."""
+    return [n for n in ("muon_hparams_default", "muon_init", "muon_workspace_size", "muon_step",
+                        "muon_plan_info", "muon_debug_gemm", "muon_profile_read", "muon_destroy",
+                        "muon_status_str")
+            if hasattr(_lib, n)]

@@ -1,0 +1,703 @@
+// C-ABI front end of the Muon update library: argument validation, the shape-adaptive
+// plan (same-shape groups, plain vs Gram NS, tile size) and the stage sequence each
+// group enqueues on the caller's stream.
+//
+// Sources: MuonX article (Baidu Baige, damodev.csdn.net), section 3.2 (Gram NS: segments
+// 2+2+1, Gram matrix rebuilt after rounds 2 and 4, transform restarted per segment; 10
+// long + 5 square products become 6 long + 11 square); DMuon summary (gist.science),
+// sections 2.2 (symmetric Gram product, batching of similar shapes) and 2.4 (per-shape
+// kernel configuration, cached); DMuon announcement (agentren.cn), improvement 2 (the
+// execution stack adapts the math form and kernels to each matrix shape).
+#include "../../include/muon.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "internal.hpp"
+
+// Stage profiler: with MUON_FLAG_PROFILE every launch is bracketed by a pair of
+// hipEvents on the launch stream; muon_profile_read aggregates them per stage and shape.
+struct ProfRecord {
+  hipEvent_t start, stop;
+  int stage;           // index into kStageNames
+  int64_t m, n;        // canonical shape of the group
+  int count;           // matrices in the launch
+  double flops, bytes; // algorithmic work of the launch
+};
+
+struct muon_ctx {
+  int device;
+  uint32_t flags;
+  int cu_count;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> event_pool;
+  std::vector<ProfRecord> records;
+  size_t next_event = 0;
+};
+
+namespace muon {
+namespace {
+
+constexpr int64_t kPad = 64;          // canonical dims are padded to multiples of 64
+constexpr int64_t kMaxDim = 1 << 20;  // per-dimension limit
+constexpr int kMaxRounds = 64;
+constexpr int kMaxBf16Segment = 8;    // fp16 transform: a^k must stay far below 65504
+constexpr int kMaxBatch = 65535;      // grid.y limit per launch
+constexpr size_t kAlign = 256;
+
+inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Group {
+  int64_t m = 0, n = 0;        // canonical m' <= n'
+  int64_t Mp = 0, Np = 0;      // padded
+  int mode = MUON_NS_GRAM;
+  int tile_sq = 64, tile_ap = 64;
+  std::vector<int> members;    // indices into the caller's list
+  int table_base = 0;          // first descriptor of this group in the table
+  // workspace offsets (bytes) and per-matrix element strides
+  size_t off_partials = 0, off_s = 0, off_x[2] = {0, 0}, off_sq[4] = {0, 0, 0, 0};
+  int64_t stride_x = 0, stride_sq = 0;
+  int mom_tiles_m = 0, mom_tiles_n = 0;
+  double work = 0.0;
+};
+
+struct Plan {
+  std::vector<Group> groups;
+  std::vector<int> group_of;   // per caller index
+  size_t off_table = 0;
+  size_t bytes = 0;
+};
+
+inline bool finite(float x) { return std::isfinite(x); }
+
+int validate_hparams(const muon_hparams* hp) {
+  if (!hp) return MUON_ERR_ARG;
+  if (!finite(hp->lr) || !finite(hp->weight_decay) || !finite(hp->eps) || hp->eps < 0.0f) return MUON_ERR_ARG;
+  if (!finite(hp->momentum) || hp->momentum < 0.0f || hp->momentum >= 1.0f) return MUON_ERR_ARG;
+  if (hp->nesterov != 0 && hp->nesterov != 1) return MUON_ERR_ARG;
+  if (!finite(hp->a) || !finite(hp->b) || !finite(hp->c)) return MUON_ERR_ARG;
+  if (hp->n_segments < 1 || hp->n_segments > MUON_MAX_SEGMENTS) return MUON_ERR_ARG;
+  int rounds = 0;
+  for (int i = 0; i < hp->n_segments; ++i) {
+    if (hp->segments[i] < 1 || hp->segments[i] > kMaxRounds) return MUON_ERR_ARG;
+    rounds += hp->segments[i];
+  }
+  if (rounds > kMaxRounds) return MUON_ERR_ARG;
+  if (hp->mode != MUON_NS_AUTO && hp->mode != MUON_NS_PLAIN && hp->mode != MUON_NS_GRAM) return MUON_ERR_ARG;
+  for (int dt : {hp->w_dtype, hp->g_dtype, hp->m_dtype, hp->ns_dtype})
+    if (dt != MUON_F32 && dt != MUON_BF16) return MUON_ERR_ARG;
+  if (hp->ns_dtype == MUON_BF16 && hp->mode != MUON_NS_PLAIN) {
+    for (int i = 0; i < hp->n_segments; ++i)
+      if (hp->segments[i] > kMaxBf16Segment) return MUON_ERR_UNSUPPORTED;
+  }
+  return MUON_OK;
+}
+
+int validate_matrix(const muon_matrix& mt, bool need_ptrs) {
+  if (mt.rows < 1 || mt.cols < 1 || mt.rows > kMaxDim || mt.cols > kMaxDim) return MUON_ERR_ARG;
+  if (need_ptrs && (!mt.W || !mt.G || !mt.M)) return MUON_ERR_ARG;
+  return MUON_OK;
+}
+
+int total_rounds(const muon_hparams& hp) {
+  int r = 0;
+  for (int i = 0; i < hp.n_segments; ++i) r += hp.segments[i];
+  return r;
+}
+
+// Matmul FLOPs as the MuonX article counts them: long = 2 m'^2 n', square = 2 m'^3.
+double dense_flops(int64_t m, int64_t n, int mode, const muon_hparams& hp) {
+  const double L = 2.0 * m * m * n, S = 2.0 * m * m * m;
+  if (mode == MUON_NS_PLAIN) {
+    const int r = total_rounds(hp);
+    return r * (2.0 * L + S);
+  }
+  double f = 0.0;
+  for (int i = 0; i < hp.n_segments; ++i) f += 2.0 * L + (4.0 * hp.segments[i] - 3.0) * S;
+  return f;
+}
+
+// FLOPs the kernels perform: symmetric outputs (X X^T and every m' x m' product, all of
+// which are symmetric in exact arithmetic) compute one triangle.
+double kernel_flops(int64_t m, int64_t n, int mode, const muon_hparams& hp) {
+  const double syrk = 1.0 * m * m * n, apply = 2.0 * m * m * n, sq = 1.0 * m * m * m;
+  if (mode == MUON_NS_PLAIN) return total_rounds(hp) * (syrk + sq + apply);
+  double f = 0.0;
+  for (int i = 0; i < hp.n_segments; ++i) f += syrk + apply + (4.0 * hp.segments[i] - 3.0) * sq;
+  return f;
+}
+
+// Shape-adaptive choice of the NS form: Gram pays when the long products it saves cost
+// more than the square ones it adds (MuonX section 3.2: benefit depends on the shape).
+int choose_mode(int64_t m, int64_t n, const muon_hparams& hp) {
+  if (hp.mode != MUON_NS_AUTO) return hp.mode;
+  return dense_flops(m, n, MUON_NS_GRAM, hp) < dense_flops(m, n, MUON_NS_PLAIN, hp) ? MUON_NS_GRAM
+                                                                                      : MUON_NS_PLAIN;
+}
+
+// Tile edge: 128 when the batch still gives every CU a couple of tiles, else 64.
+int choose_tile(int64_t tiles128, int64_t count, int cu) {
+  return (tiles128 * count >= 2LL * cu) ? 128 : 64;
+}
+
+int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams& hp,
+               bool need_ptrs, Plan& plan) {
+  plan = Plan{};
+  plan.group_of.assign(count, -1);
+  std::map<std::tuple<int64_t, int64_t>, std::vector<int>> keyed;
+  for (int i = 0; i < count; ++i) {
+    const int rc = validate_matrix(mats[i], need_ptrs);
+    if (rc != MUON_OK) return rc;
+    const int64_t m = std::min(mats[i].rows, mats[i].cols), n = std::max(mats[i].rows, mats[i].cols);
+    keyed[{m, n}].push_back(i);
+  }
+  const bool f32 = hp.ns_dtype == MUON_F32;
+  const size_t ex = f32 ? 4 : 2, esq = f32 ? 4 : 2;
+  for (auto& kv : keyed) {
+    const int64_t m = std::get<0>(kv.first), n = std::get<1>(kv.first);
+    const std::vector<int>& all = kv.second;
+    for (size_t b = 0; b < all.size(); b += kMaxBatch) {
+      Group g;
+      g.m = m; g.n = n;
+      g.Mp = round_up(m, kPad); g.Np = round_up(n, kPad);
+      g.mode = choose_mode(m, n, hp);
+      g.members.assign(all.begin() + b, all.begin() + std::min(all.size(), b + kMaxBatch));
+      const int64_t cnt = static_cast<int64_t>(g.members.size());
+      const int64_t nt_sq = (g.Mp + 127) / 128;
+      g.tile_sq = choose_tile(nt_sq * (nt_sq + 1) / 2, cnt, ctx->cu_count);
+      g.tile_ap = choose_tile(((g.Mp + 127) / 128) * ((g.Np + 127) / 128), cnt, ctx->cu_count);
+      g.work = kernel_flops(m, n, g.mode, hp) * cnt;
+      plan.groups.push_back(std::move(g));
+    }
+  }
+  // Largest work first: the big launches start while the host still enqueues the rest.
+  std::stable_sort(plan.groups.begin(), plan.groups.end(),
+                   [](const Group& a, const Group& b) { return a.work > b.work; });
+  size_t off = 0;
+  plan.off_table = off;
+  off = align_up(off + sizeof(MatDesc) * static_cast<size_t>(count));
+  int tb = 0;
+  for (size_t gi = 0; gi < plan.groups.size(); ++gi) {
+    Group& g = plan.groups[gi];
+    const size_t cnt = g.members.size();
+    g.table_base = tb;
+    tb += static_cast<int>(cnt);
+    for (int i : g.members) plan.group_of[i] = static_cast<int>(gi);
+    g.mom_tiles_m = static_cast<int>(g.Mp / 64);
+    g.mom_tiles_n = static_cast<int>(g.Np / 64);
+    g.off_partials = off;
+    off = align_up(off + sizeof(float) * cnt * g.mom_tiles_m * g.mom_tiles_n);
+    g.off_s = off;
+    off = align_up(off + sizeof(float) * cnt);
+    g.stride_x = g.Mp * g.Np;
+    for (int k = 0; k < 2; ++k) {
+      g.off_x[k] = off;
+      off = align_up(off + ex * static_cast<size_t>(g.stride_x) * cnt);
+    }
+    g.stride_sq = g.Mp * g.Mp;
+    const int nsq = (g.mode == MUON_NS_GRAM) ? 4 : 2;
+    for (int k = 0; k < nsq; ++k) {
+      g.off_sq[k] = off;
+      off = align_up(off + esq * static_cast<size_t>(g.stride_sq) * cnt);
+    }
+  }
+  plan.bytes = off;
+  return MUON_OK;
+}
+
+// ---- stage helpers ----
+struct StepEnv {
+  char* ws;
+  hipStream_t st;
+  bool f32;
+  const muon_hparams* hp;
+  muon_ctx* ctx;
+};
+
+constexpr const char* kStageNames[] = {"table", "momentum", "norm_finalize", "syrk", "square",
+                                       "apply", "apply_update"};
+enum Stage { ST_TABLE, ST_MOMENTUM, ST_FINALIZE, ST_SYRK, ST_SQUARE, ST_APPLY, ST_UPDATE };
+constexpr size_t kMaxRecords = 1 << 16;
+
+// Brackets one launch with events when profiling is on (no effect otherwise).
+struct StageTimer {
+  muon_ctx* ctx = nullptr;
+  hipStream_t st = nullptr;
+  ProfRecord rec{};
+  bool on = false;
+  StageTimer(muon_ctx* c, hipStream_t s, int stage, int64_t m, int64_t n, int count, double flops,
+             double bytes) {
+    if (!c || !(c->flags & MUON_FLAG_PROFILE) || c->records.size() >= kMaxRecords) return;
+    if (c->next_event == c->event_pool.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      c->event_pool.emplace_back(a, b);
+    }
+    const auto ev = c->event_pool[c->next_event];
+    if (hipEventRecord(ev.first, s) != hipSuccess) return;
+    ctx = c; st = s; on = true;
+    rec = ProfRecord{ev.first, ev.second, stage, m, n, count, flops, bytes};
+  }
+  void done() {
+    if (!on) return;
+    if (hipEventRecord(rec.stop, st) == hipSuccess) {
+      ctx->records.push_back(rec);
+      ++ctx->next_event;
+    }
+    on = false;
+  }
+};
+
+inline float pow2_near(double x, int lo, int hi) {
+  int e = static_cast<int>(std::lround(std::log2(std::max(x, 1.0))));
+  e = std::max(lo, std::min(hi, e));
+  return std::ldexp(1.0f, e);
+}
+
+GemmParams base_params(const Group& g, const StepEnv& env) {
+  GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.count = static_cast<int32_t>(g.members.size());
+  p.s = reinterpret_cast<const float*>(env.ws + g.off_s);
+  p.alpha = 1.0f;
+  p.Mvalid = static_cast<int32_t>(g.m);
+  p.Nvalid = static_cast<int32_t>(g.n);
+  return p;
+}
+
+void set_sym_tiles(GemmParams& p, int64_t Mp, int tile) {
+  const int nt = static_cast<int>((Mp + tile - 1) / tile);
+  p.tiles_m = p.tiles_n = nt;
+  p.tiles = nt * (nt + 1) / 2;
+}
+
+hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, float alpha, int spow) {
+  GemmParams p = base_params(g, env);
+  p.A = X; p.B = X; p.C = R;
+  p.lda = p.ldb = g.Np; p.ldc = g.Mp;
+  p.sA = p.sB = g.stride_x; p.sC = g.stride_sq;
+  p.M = p.N = static_cast<int32_t>(g.Mp); p.K = static_cast<int32_t>(g.Np);
+  p.alpha = alpha; p.alpha_spow = spow;
+  set_sym_tiles(p, g.Mp, g.tile_sq);
+  const double cnt = static_cast<double>(p.count);
+  StageTimer tm(env.ctx, env.st, ST_SYRK, g.m, g.n, p.count, cnt * g.m * g.m * g.n, 0.0);
+  const hipError_t e = launch_gemm(OP_SYRK, env.f32, g.tile_sq, p, env.st);
+  tm.done();
+  return e;
+}
+
+// C = alpha * A B^T + beta * E + gamma * I, every operand m' x m' and symmetric.
+hipError_t square(const Group& g, const StepEnv& env, const void* A, const void* B, const void* E,
+                  void* C, float alpha, float beta, float gamma) {
+  GemmParams p = base_params(g, env);
+  p.A = A; p.B = B; p.C = C; p.E = E;
+  p.lda = p.ldb = p.ldc = p.lde = g.Mp;
+  p.sA = p.sB = p.sC = p.sE = g.stride_sq;
+  p.M = p.N = p.K = static_cast<int32_t>(g.Mp);
+  p.alpha = alpha; p.beta = beta; p.gamma = gamma;
+  set_sym_tiles(p, g.Mp, g.tile_sq);
+  const double cnt = static_cast<double>(p.count);
+  StageTimer tm(env.ctx, env.st, ST_SQUARE, g.m, g.n, p.count, cnt * g.m * g.m * g.m, 0.0);
+  const hipError_t e = launch_gemm(OP_SQUARE, env.f32, g.tile_sq, p, env.st);
+  tm.done();
+  return e;
+}
+
+// Xout = alpha * Q (bscale X) + beta X   (or the fused weight update when `update`).
+hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* X, void* Xout,
+                 float alpha, float bscale, int bspow, float beta, int beta_spow, bool use_e,
+                 bool update, const MatDesc* table) {
+  GemmParams p = base_params(g, env);
+  p.A = Q; p.B = X; p.C = Xout; p.E = use_e ? X : nullptr;
+  p.lda = g.Mp; p.ldb = g.Np; p.ldc = g.Np; p.lde = g.Np;
+  p.sA = g.stride_sq; p.sB = g.stride_x; p.sC = g.stride_x; p.sE = g.stride_x;
+  p.M = static_cast<int32_t>(g.Mp); p.N = static_cast<int32_t>(g.Np); p.K = static_cast<int32_t>(g.Mp);
+  p.alpha = alpha; p.bscale = bscale; p.bscale_spow = bspow;
+  p.beta = beta; p.beta_spow = beta_spow;
+  const int t = g.tile_ap;
+  p.tiles_m = static_cast<int32_t>((g.Mp + t - 1) / t);
+  p.tiles_n = static_cast<int32_t>((g.Np + t - 1) / t);
+  p.tiles = p.tiles_m * p.tiles_n;
+  if (update) {
+    p.table = table;
+    p.lr = env.hp->lr;
+    p.wd = env.hp->weight_decay;
+    p.w_bf16 = env.hp->w_dtype == MUON_BF16;
+  }
+  const double cnt = static_cast<double>(p.count);
+  const double wbytes = update ? cnt * g.m * g.n * 2.0 * (p.w_bf16 ? 2.0 : 4.0) : 0.0;
+  StageTimer tm(env.ctx, env.st, update ? ST_UPDATE : ST_APPLY, g.m, g.n, p.count,
+                cnt * 2.0 * g.m * g.m * g.n, wbytes);
+  const hipError_t e = launch_gemm(update ? OP_UPDATE : OP_APPLY, env.f32, t, p, env.st);
+  tm.done();
+  return e;
+}
+
+#define MUON_HIP(call)                       \
+  do {                                       \
+    if ((call) != hipSuccess) return MUON_ERR_HIP; \
+  } while (0)
+
+int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
+  const muon_hparams& hp = *env.hp;
+  const bool f32 = env.f32;
+  // Momentum, canonical U (into X buffer 0) and per-tile partial sums of squares.
+  MomentumParams mp;
+  std::memset(&mp, 0, sizeof(mp));
+  mp.table = table;
+  mp.U = env.ws + g.off_x[0];
+  mp.sU = g.stride_x; mp.ldu = g.Np;
+  mp.m = static_cast<int32_t>(g.m); mp.n = static_cast<int32_t>(g.n);
+  mp.Mp = static_cast<int32_t>(g.Mp); mp.Np = static_cast<int32_t>(g.Np);
+  mp.tiles_m = g.mom_tiles_m; mp.tiles_n = g.mom_tiles_n;
+  mp.count = static_cast<int32_t>(g.members.size());
+  mp.mu = hp.momentum; mp.nesterov = hp.nesterov;
+  mp.g_bf16 = hp.g_dtype == MUON_BF16; mp.m_bf16 = hp.m_dtype == MUON_BF16; mp.u_bf16 = !f32;
+  mp.partials = reinterpret_cast<float*>(env.ws + g.off_partials);
+  {
+    // algorithmic bytes: G read, M read + write, U written (canonical, padded)
+    const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;
+    const double ub = f32 ? 4.0 : 2.0;
+    const double elems = static_cast<double>(mp.count) * g.m * g.n;
+    StageTimer tm(env.ctx, env.st, ST_MOMENTUM, g.m, g.n, mp.count, 0.0,
+                  elems * (gb + 2.0 * mb + ub));
+    MUON_HIP(launch_momentum(mp, env.st));
+    tm.done();
+  }
+  {
+    StageTimer tm(env.ctx, env.st, ST_FINALIZE, g.m, g.n, mp.count, 0.0,
+                  4.0 * mp.count * g.mom_tiles_m * g.mom_tiles_n);
+    MUON_HIP(launch_norm_finalize(mp.partials, g.mom_tiles_m * g.mom_tiles_n, mp.count, hp.eps,
+                                  reinterpret_cast<float*>(env.ws + g.off_s), env.st));
+    tm.done();
+  }
+
+  // Scales of the bf16 path: Gram-like matrices (R, Q R, A) are kept multiplied by
+  // e ~ m' so their entries sit in fp16's normal range; the long operand X enters the
+  // fp16 apply multiplied by xs ~ sqrt(m' n') (both powers of two, so exact).
+  const float e = f32 ? 1.0f : pow2_near(static_cast<double>(g.m), 0, 14);
+  const float xs = f32 ? 1.0f : pow2_near(std::sqrt(static_cast<double>(g.m) * g.n), 0, 14);
+  const float a = hp.a, b1 = hp.b / e, c1 = hp.c / (e * e);
+
+  void* X[2] = {env.ws + g.off_x[0], env.ws + g.off_x[1]};
+  int cur = 0;
+  if (g.mode == MUON_NS_PLAIN) {
+    void* A = env.ws + g.off_sq[0];
+    void* B = env.ws + g.off_sq[1];
+    const int rounds = total_rounds(hp);
+    for (int r = 0; r < rounds; ++r) {
+      const bool first = r == 0, last = r == rounds - 1;
+      MUON_HIP(syrk(g, env, X[cur], A, e, first ? 2 : 0));
+      MUON_HIP(square(g, env, A, A, A, B, c1, b1, 0.0f));
+      MUON_HIP(apply(g, env, B, X[cur], X[cur ^ 1], 1.0f / xs, xs, first ? 1 : 0, a, first ? 1 : 0,
+                     true, last, table));
+      cur ^= 1;
+    }
+  } else {
+    void* R = env.ws + g.off_sq[0];
+    void* Q = env.ws + g.off_sq[1];
+    void* T1 = env.ws + g.off_sq[2];
+    void* T2 = env.ws + g.off_sq[3];
+    for (int sgi = 0; sgi < hp.n_segments; ++sgi) {
+      const bool first = sgi == 0, last = sgi == hp.n_segments - 1;
+      MUON_HIP(syrk(g, env, X[cur], R, e, first ? 2 : 0));
+      MUON_HIP(square(g, env, R, R, R, Q, c1, b1, a));            // Q = P(R)
+      for (int k = 1; k < hp.segments[sgi]; ++k) {
+        MUON_HIP(square(g, env, Q, R, nullptr, T1, 1.0f, 0.0f, 0.0f));   // T = Q R
+        MUON_HIP(square(g, env, T1, Q, nullptr, T2, 1.0f, 0.0f, 0.0f));  // A = T Q^T
+        MUON_HIP(square(g, env, T2, T2, T2, T1, c1, b1, a));             // P = aI + bA + cA^2
+        MUON_HIP(square(g, env, T1, Q, nullptr, T2, 1.0f, 0.0f, 0.0f));  // Q <- P Q
+        std::swap(Q, T2);
+      }
+      MUON_HIP(apply(g, env, Q, X[cur], X[cur ^ 1], 1.0f / xs, xs, first ? 1 : 0, 0.0f, 0, false,
+                     last, table));
+      cur ^= 1;
+    }
+  }
+  return MUON_OK;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(dev) == hipSuccess) ok = true;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+void muon_hparams_default(muon_hparams* hp) {
+  if (!hp) return;
+  std::memset(hp, 0, sizeof(*hp));
+  hp->lr = 0.02f;
+  hp->momentum = 0.95f;
+  hp->weight_decay = 0.0f;
+  hp->eps = 1e-7f;
+  hp->nesterov = 1;
+  hp->a = 3.4445f;
+  hp->b = -4.7750f;
+  hp->c = 2.0315f;
+  hp->n_segments = 3;
+  hp->segments[0] = 2;
+  hp->segments[1] = 2;
+  hp->segments[2] = 1;
+  hp->mode = MUON_NS_AUTO;
+  hp->w_dtype = MUON_F32;
+  hp->g_dtype = MUON_BF16;
+  hp->m_dtype = MUON_BF16;
+  hp->ns_dtype = MUON_BF16;
+}
+
+int muon_init(muon_ctx** out, int device, uint32_t flags) {
+  try {
+    if (!out) return MUON_ERR_ARG;
+    *out = nullptr;
+    if ((flags & ~(MUON_FLAG_MODEL_ONLY | MUON_FLAG_PROFILE)) != 0) return MUON_ERR_ARG;
+    if (device == -1) {  // host-only context: planning and validation, no launches
+      muon_ctx* c = new (std::nothrow) muon_ctx;
+      if (!c) return MUON_ERR_HIP;
+      c->device = -1;
+      c->flags = flags;
+      c->cu_count = 256;
+      *out = c;
+      return MUON_OK;
+    }
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess) return MUON_ERR_DEVICE;
+    if (device < 0 || device >= n) return MUON_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return MUON_ERR_DEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MUON_ERR_DEVICE;
+    muon_ctx* c = new (std::nothrow) muon_ctx;
+    if (!c) return MUON_ERR_HIP;
+    c->device = device;
+    c->flags = flags;
+    c->cu_count = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+    *out = c;
+    return MUON_OK;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+int muon_workspace_size(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams* hp,
+                        size_t* bytes) {
+  try {
+    if (!ctx || !bytes || count < 0 || (count > 0 && !mats)) return MUON_ERR_ARG;
+    const int rc = validate_hparams(hp);
+    if (rc != MUON_OK) return rc;
+    Plan plan;
+    const int pc = build_plan(ctx, mats, count, *hp, false, plan);
+    if (pc != MUON_OK) return pc;
+    *bytes = count == 0 ? 0 : plan.bytes;
+    return MUON_OK;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams* hp,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!ctx || count < 0 || (count > 0 && !mats)) return MUON_ERR_ARG;
+    const int rc = validate_hparams(hp);
+    if (rc != MUON_OK) return rc;
+    if (count == 0) return MUON_OK;
+    Plan plan;
+    const int pc = build_plan(ctx, mats, count, *hp, true, plan);
+    if (pc != MUON_OK) return pc;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 ||
+        workspace_bytes < plan.bytes)
+      return MUON_ERR_WORKSPACE;
+    if (ctx->device < 0) return MUON_ERR_DEVICE;
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return MUON_ERR_HIP;
+    StepEnv env{static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
+                hp->ns_dtype == MUON_F32, hp, ctx};
+    MatDesc* table = reinterpret_cast<MatDesc*>(env.ws + plan.off_table);
+    // Descriptor table, ordered by group, written by small kernels (no host sync).
+    std::vector<MatDesc> descs(count);
+    for (const Group& g : plan.groups) {
+      for (size_t i = 0; i < g.members.size(); ++i) {
+        const muon_matrix& mt = mats[g.members[i]];
+        MatDesc d{};
+        d.W = mt.W; d.G = mt.G; d.M = mt.M;
+        d.rows = mt.rows; d.cols = mt.cols;
+        d.transposed = mt.rows > mt.cols ? 1 : 0;
+        descs[g.table_base + i] = d;
+      }
+    }
+    for (int b = 0; b < count; b += kTableChunk) {
+      TableChunk c;
+      std::memset(&c, 0, sizeof(c));
+      c.n = std::min(kTableChunk, count - b);
+      for (int i = 0; i < c.n; ++i) c.d[i] = descs[b + i];
+      StageTimer tm(ctx, env.st, ST_TABLE, 0, 0, c.n, 0.0, sizeof(MatDesc) * c.n);
+      MUON_HIP(launch_write_table(c, table + b, env.st));
+      tm.done();
+    }
+    for (const Group& g : plan.groups) {
+      const int r = run_group(g, env, table + g.table_base);
+      if (r != MUON_OK) return r;
+    }
+    return MUON_OK;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams* hp,
+                   int index, muon_plan_entry* out) {
+  try {
+    if (!ctx || !out || !mats || count <= 0 || index < 0 || index >= count) return MUON_ERR_ARG;
+    const int rc = validate_hparams(hp);
+    if (rc != MUON_OK) return rc;
+    Plan plan;
+    const int pc = build_plan(ctx, mats, count, *hp, false, plan);
+    if (pc != MUON_OK) return pc;
+    const Group& g = plan.groups[plan.group_of[index]];
+    out->mode = g.mode;
+    out->transposed = mats[index].rows > mats[index].cols ? 1 : 0;
+    out->m = g.m;
+    out->n = g.n;
+    out->group = plan.group_of[index];
+    out->tile = g.tile_ap;
+    out->dense_flops = dense_flops(g.m, g.n, g.mode, *hp);
+    out->kernel_flops = kernel_flops(g.m, g.n, g.mode, *hp);
+    return MUON_OK;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+int muon_debug_gemm(muon_ctx* ctx, int kind, int ns_dtype, int tile, int64_t M, int64_t N, int64_t K,
+                    const void* A, const void* B, const void* E, void* C, float alpha, float beta,
+                    float gamma, float bscale, void* stream) {
+  try {
+    if (!ctx || !A || !B || !C) return MUON_ERR_ARG;
+    if (kind < 0 || kind > 2 || (ns_dtype != MUON_F32 && ns_dtype != MUON_BF16)) return MUON_ERR_ARG;
+    if (tile != 64 && tile != 128) return MUON_ERR_ARG;
+    if (M < 64 || N < 64 || K < 64 || M % 64 || N % 64 || K % 64 || M > kMaxDim || N > kMaxDim ||
+        K > kMaxDim)
+      return MUON_ERR_ARG;
+    if ((kind == 0 || kind == 1) && M != N) return MUON_ERR_ARG;
+    if (ctx->device < 0) return MUON_ERR_DEVICE;
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return MUON_ERR_HIP;
+    GemmParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.count = 1;
+    p.A = A; p.B = B; p.C = C; p.E = E;
+    p.M = static_cast<int32_t>(M); p.N = static_cast<int32_t>(N); p.K = static_cast<int32_t>(K);
+    p.Mvalid = p.M; p.Nvalid = p.N;
+    p.alpha = alpha; p.beta = beta; p.gamma = gamma; p.bscale = bscale;
+    GemmOp op;
+    if (kind == 2) {
+      op = OP_APPLY;
+      p.lda = K; p.ldb = N; p.ldc = N; p.lde = N;
+      p.tiles_m = static_cast<int32_t>((M + tile - 1) / tile);
+      p.tiles_n = static_cast<int32_t>((N + tile - 1) / tile);
+      p.tiles = p.tiles_m * p.tiles_n;
+    } else {
+      op = kind == 0 ? OP_SYRK : OP_SQUARE;
+      if (kind == 0) B = A, p.B = A;
+      p.lda = K; p.ldb = K; p.ldc = N; p.lde = N;
+      const int nt = static_cast<int>((M + tile - 1) / tile);
+      p.tiles_m = p.tiles_n = nt;
+      p.tiles = nt * (nt + 1) / 2;
+    }
+    if (launch_gemm(op, ns_dtype == MUON_F32, tile, p, static_cast<hipStream_t>(stream)) != hipSuccess)
+      return MUON_ERR_HIP;
+    return MUON_OK;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+int muon_profile_read(muon_ctx* ctx, muon_profile_entry* out, int capacity, int* n_out) {
+  try {
+    if (!ctx || !n_out || capacity < 0 || (capacity > 0 && !out)) return MUON_ERR_ARG;
+    *n_out = 0;
+    if (!(ctx->flags & MUON_FLAG_PROFILE)) return MUON_ERR_ARG;
+    if (ctx->records.empty()) return MUON_OK;
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return MUON_ERR_HIP;
+    if (hipEventSynchronize(ctx->records.back().stop) != hipSuccess) return MUON_ERR_HIP;
+    std::map<std::tuple<int, int64_t, int64_t, int>, muon_profile_entry> agg;
+    std::vector<std::tuple<int, int64_t, int64_t, int>> order;
+    for (const ProfRecord& r : ctx->records) {
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return MUON_ERR_HIP;
+      const auto key = std::make_tuple(r.stage, r.m, r.n, r.count);
+      auto it = agg.find(key);
+      if (it == agg.end()) {
+        muon_profile_entry e;
+        std::memset(&e, 0, sizeof(e));
+        std::strncpy(e.stage, kStageNames[r.stage], sizeof(e.stage) - 1);
+        e.m = r.m; e.n = r.n; e.count = r.count;
+        it = agg.emplace(key, e).first;
+        order.push_back(key);
+      }
+      it->second.launches += 1;
+      it->second.total_ms += ms;
+      it->second.flops += r.flops;
+      it->second.bytes += r.bytes;
+    }
+    ctx->records.clear();
+    ctx->next_event = 0;
+    int n = 0;
+    for (const auto& k : order) {
+      if (n < capacity) out[n] = agg[k];
+      ++n;
+    }
+    *n_out = n;
+    return n > capacity ? MUON_ERR_ARG : MUON_OK;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+int muon_destroy(muon_ctx* ctx) {
+  if (!ctx) return MUON_OK;
+  if (ctx->device >= 0 && !ctx->event_pool.empty()) {
+    DeviceGuard dg(ctx->device);
+    for (auto& ev : ctx->event_pool) {
+      (void)hipEventDestroy(ev.first);
+      (void)hipEventDestroy(ev.second);
+    }
+  }
+  delete ctx;
+  return MUON_OK;
+}
+
+const char* muon_status_str(int status) {
+  switch (status) {
+    case MUON_OK: return "MUON_OK: success";
+    case MUON_ERR_ARG: return "MUON_ERR_ARG: invalid argument";
+    case MUON_ERR_WORKSPACE: return "MUON_ERR_WORKSPACE: workspace null, misaligned or too small";
+    case MUON_ERR_DEVICE: return "MUON_ERR_DEVICE: invalid device or not gfx950";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP: HIP runtime or launch failure";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED: request not implemented";
+    default: return "unknown muon status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal interfaces between the C-ABI front end (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace muon {
+
+// Per-matrix descriptor, written into the workspace at the start of every step.
+struct MatDesc {
+  void* W;
+  const void* G;
+  void* M;
+  int64_t rows, cols;     // stored shape (row-major, ld = cols)
+  int32_t transposed;     // 1: canonical X is the transpose of the stored matrix
+  int32_t pad_;
+};
+
+enum Kind : int { KIND_BF16 = 0, KIND_F16 = 1, KIND_F32 = 2 };
+enum Epi : int { EPI_STORE = 0, EPI_UPDATE = 1 };
+
+// Batched GEMM over `count` same-shape problems. Matrix i of the batch uses
+// A + i*sA, B + i*sB, C + i*sC, E + i*sE (element strides) and scalar s[i].
+//   NT (B is N x K row-major):  acc = A * B^T
+//   NN (B is K x N row-major):  acc = A * (bscale' * B)   (B converted to A's type)
+// Epilogue: out = alpha' * acc + beta' * E + gamma * [row == col]
+//   with alpha' = alpha * s[i]^alpha_spow, beta' = beta * s[i]^beta_spow,
+//   bscale' = bscale * s[i]^bscale_spow.
+// SYM: only tiles with tile_m <= tile_n are computed; off-diagonal tiles are also
+// stored mirrored, so C is exactly symmetric.
+// EPI_UPDATE: out is O in canonical orientation; W[desc] <- W*(1 - lr*wd) - lr*O for
+// row < Mvalid, col < Nvalid, through the descriptor's orientation.
+struct GemmParams {
+  const void* A; const void* B; void* C; const void* E;
+  int64_t lda, ldb, ldc, lde;
+  int64_t sA, sB, sC, sE;
+  int32_t M, N, K;
+  int32_t Mvalid, Nvalid;
+  int32_t tiles_m, tiles_n, tiles;
+  int32_t count;
+  float alpha, beta, gamma, bscale;
+  int32_t alpha_spow, beta_spow, bscale_spow;
+  const float* s;
+  const MatDesc* table;   // EPI_UPDATE: descriptors of the batch (entry i = matrix i)
+  float lr, wd;
+  int32_t w_bf16;
+};
+
+// Stage identifiers of the GEMM family.
+enum GemmOp : int {
+  OP_SYRK = 0,     // C = X X^T, symmetric (NT, A = B = X)
+  OP_SQUARE = 1,   // C = A B^T with symmetric output (NT)
+  OP_APPLY = 2,    // C = A B (NN), general output
+  OP_UPDATE = 3,   // as OP_APPLY, epilogue updates W
+};
+
+// Launch one batched GEMM stage. ns_f32: fp32 kernels, else bf16/fp16 kernels.
+hipError_t launch_gemm(GemmOp op, bool ns_f32, int tile, const GemmParams& p, hipStream_t st);
+
+// Momentum + canonical-orientation write of U + per-block partial sums of U^2.
+struct MomentumParams {
+  const MatDesc* table;   // entry i = matrix i of the batch
+  void* U;                // canonical padded buffers, matrix i at U + i*sU (elements)
+  int64_t sU, ldu;        // element stride between matrices, leading dimension (= Np)
+  int32_t m, n;           // canonical dims m' <= n'
+  int32_t Mp, Np;         // padded canonical dims
+  int32_t tiles_m, tiles_n;  // 64 x 64 canonical tiles per matrix
+  int32_t count;
+  float mu;
+  int32_t nesterov;
+  int32_t g_bf16, m_bf16, u_bf16;   // storage dtypes (0: fp32)
+  float* partials;        // [count][tiles_m*tiles_n]
+};
+hipError_t launch_momentum(const MomentumParams& p, hipStream_t st);
+
+// s[i] = 1 / (sqrt(sum_j partials[i][j]) + eps), fixed-order fp64 reduction.
+hipError_t launch_norm_finalize(const float* partials, int per_matrix, int count, float eps,
+                                float* s, hipStream_t st);
+
+// Copy up to kTableChunk descriptors (passed by value) into device memory.
+constexpr int kTableChunk = 48;
+struct TableChunk {
+  MatDesc d[kTableChunk];
+  int32_t n;
+};
+hipError_t launch_write_table(const TableChunk& c, MatDesc* dst, hipStream_t st);
+
+}  // namespace muon

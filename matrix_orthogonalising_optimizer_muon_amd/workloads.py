@@ -161,3 +161,27 @@ def custom(name: str, shapes, *, structure="gaussian", dtype="bf16", rank=8, dec
                     g_dtype="f32" if f32 else "bf16", m_dtype="f32" if f32 else "bf16",
                     w_dtype="f32", ns_dtype="f32" if f32 else "bf16", structure=structure,
                     rank=rank, decay=decay, steps=steps)
+
+
+def gradient_torch(w: Workload, step: int, index: int, device="cuda", spec: MatrixSpec | None = None):
+    """Device-side draw with the same recipe as :func:`gradient_np` (torch's generator,
+    so not the same values): for timing runs of workloads too large to draw on the host.
+    Returns a tensor in the gradient's storage dtype."""
+    import torch
+
+    spec = spec or w.matrices[index]
+    rows, cols = spec.rows, spec.cols
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(np.random.SeedSequence([w.wid, step, index, 7]).generate_state(1)[0]))
+    if w.structure == "gaussian":
+        G = torch.randn(rows, cols, generator=gen, device=device)
+    else:
+        r = min(w.rank, rows, cols)
+        Ub, Rb = torch.linalg.qr(torch.randn(rows, r, generator=gen, device=device))
+        Ub = Ub * torch.sign(torch.diagonal(Rb))
+        Vb, Rv = torch.linalg.qr(torch.randn(cols, r, generator=gen, device=device))
+        Vb = Vb * torch.sign(torch.diagonal(Rv))
+        s = w.scale * torch.arange(1, r + 1, device=device, dtype=torch.float32) ** (-w.decay)
+        G = (Ub * s) @ Vb.T
+        G += w.noise * torch.randn(rows, cols, generator=gen, device=device)
+    return G.to(torch.bfloat16 if w.g_dtype == "bf16" else torch.float32)

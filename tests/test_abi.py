@@ -1,0 +1,225 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the header
+declares, validates every argument before touching a device, and plans as documented.
+
+A host-only context (device -1) makes planning and validation callable on the CPU.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from oracle import flop_model
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+B = pytest.importorskip("matrix_orthogonalising_optimizer_muon_amd.binding")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert "muon_step" in names and "muon_init" in names and len(names) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (muon_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ["MUON_OK", "MUON_ERR_ARG", "MUON_ERR_WORKSPACE", "MUON_ERR_DEVICE", "MUON_ERR_HIP",
+                 "MUON_ERR_UNSUPPORTED", "MUON_F32", "MUON_BF16", "MUON_NS_AUTO", "MUON_NS_PLAIN",
+                 "MUON_NS_GRAM", "MUON_MAX_SEGMENTS"]:
+        m = re.search(rf"#define {name} (-?\d+)", text)
+        assert m and int(m.group(1)) == getattr(B, name), name
+
+
+def test_struct_layouts_match_c_compiler(tmp_path):
+    """Field offsets and sizes of the header's structs, as gcc lays them out, equal the
+    ctypes mirrors the binding uses."""
+    structs = {"muon_matrix": B.muon_matrix, "muon_hparams": B.muon_hparams,
+               "muon_plan_entry": B.muon_plan_entry, "muon_profile_entry": B.muon_profile_entry}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
+    for name, cls in structs.items():
+        lines.append(f'printf("{name} size %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{name} {f} %zu\\n", offsetof({name}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        name, field, val = line.split()
+        got[(name, field)] = int(val)
+    for name, cls in structs.items():
+        assert got[(name, "size")] == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert got[(name, f)] == getattr(cls, f).offset, (name, f)
+
+
+def test_defaults_and_status_strings():
+    hp = B.muon_hparams_default()
+    assert abs(hp.lr - 0.02) < 1e-9 and abs(hp.momentum - 0.95) < 1e-7 and hp.nesterov == 1
+    assert (round(hp.a, 4), round(hp.b, 4), round(hp.c, 4)) == (3.4445, -4.775, 2.0315)
+    assert hp.n_segments == 3 and list(hp.segments)[:3] == [2, 2, 1]
+    assert hp.mode == B.MUON_NS_AUTO and hp.w_dtype == B.MUON_F32 and hp.ns_dtype == B.MUON_BF16
+    for s in [0, -1, -2, -3, -4, -5]:
+        assert B.muon_status_str(s).startswith("MUON_")
+    assert "unknown" in B.muon_status_str(42)
+
+
+@pytest.fixture(scope="module")
+def hctx():
+    ctx = B.muon_init(-1)
+    yield ctx
+    B.muon_destroy(ctx)
+
+
+FAKE = 0x10000  # never dereferenced: host-only contexts launch nothing
+
+
+def mats_of(shapes):
+    return B.matrix_list([(FAKE, FAKE, FAKE, r, c) for r, c in shapes])
+
+
+def step(ctx, shapes, hp=None, ws=FAKE * 256, wsb=1 << 40, count=None):
+    hp = hp or B.make_hparams()
+    arr = mats_of(shapes)
+    n = len(shapes) if count is None else count
+    return B._lib.muon_step(ctx, arr, n, ctypes.byref(hp), ctypes.c_void_p(ws), ctypes.c_size_t(wsb), None)
+
+
+def test_profile_read_errors(hctx):
+    n = ctypes.c_int(-1)
+    buf = (B.muon_profile_entry * 4)()
+    # context without the profiling flag
+    assert B._lib.muon_profile_read(hctx, buf, 4, ctypes.byref(n)) == B.MUON_ERR_ARG
+    assert B._lib.muon_profile_read(None, buf, 4, ctypes.byref(n)) == B.MUON_ERR_ARG
+    pctx = B.muon_init(-1, B.MUON_FLAG_PROFILE)
+    assert B.muon_profile_read(pctx) == []
+    B.muon_destroy(pctx)
+
+
+def test_init_errors():
+    out = ctypes.c_void_p()
+    assert B._lib.muon_init(None, 0, 0) == B.MUON_ERR_ARG
+    assert B._lib.muon_init(ctypes.byref(out), -1, 4) == B.MUON_ERR_ARG
+    assert B._lib.muon_init(ctypes.byref(out), 9999, 0) == B.MUON_ERR_DEVICE
+    assert B._lib.muon_destroy(None) == B.MUON_OK
+
+
+def test_validation_before_device(hctx):
+    ok_shapes = [(64, 256)]
+    # valid arguments reach the device check
+    assert step(hctx, ok_shapes) == B.MUON_ERR_DEVICE
+    assert step(hctx, [], count=0) == B.MUON_OK           # empty list is a no-op
+    assert B._lib.muon_step(None, None, 0, None, None, 0, None) == B.MUON_ERR_ARG
+    assert step(hctx, ok_shapes, count=-1) == B.MUON_ERR_ARG
+    assert step(hctx, [(0, 256)]) == B.MUON_ERR_ARG
+    assert step(hctx, [(64, -3)]) == B.MUON_ERR_ARG
+    assert step(hctx, [(1 << 21, 4)]) == B.MUON_ERR_ARG
+    arr = B.matrix_list([(0, FAKE, FAKE, 64, 256)])
+    hp = B.make_hparams()
+    assert B._lib.muon_step(hctx, arr, 1, ctypes.byref(hp), ctypes.c_void_p(FAKE * 256),
+                            ctypes.c_size_t(1 << 40), None) == B.MUON_ERR_ARG
+    bad = [dict(momentum=1.0), dict(momentum=-0.1), dict(eps=-1.0), dict(lr=float("nan")),
+           dict(nesterov=2), dict(coeffs=(float("inf"), 0, 0)), dict(segments=[]),
+           dict(segments=[2, 0, 1]), dict(segments=[1] * 9), dict(segments=[40, 30]),
+           dict(mode=7), dict(w_dtype=5), dict(g_dtype=-1), dict(m_dtype=2), dict(ns_dtype=9)]
+    for kw in bad:
+        hp = B.make_hparams(**kw)
+        if kw.get("segments") == []:
+            hp.n_segments = 0
+        assert step(hctx, ok_shapes, hp) == B.MUON_ERR_ARG, kw
+    # fp16 transform limit: a Gram segment longer than 8 rounds on the bf16 path
+    assert step(hctx, ok_shapes, B.make_hparams(segments=[9], mode="gram")) == B.MUON_ERR_UNSUPPORTED
+    assert step(hctx, ok_shapes, B.make_hparams(segments=[9], mode="plain")) == B.MUON_ERR_DEVICE
+    assert step(hctx, ok_shapes, B.make_hparams(segments=[9], mode="gram", ns_dtype="f32")) == B.MUON_ERR_DEVICE
+
+
+def test_workspace_errors(hctx):
+    shapes = [(64, 256), (300, 70)]
+    need = B.muon_workspace_size(hctx, [(0, 0, 0, r, c) for r, c in shapes], B.make_hparams())
+    assert need > 0 and need % 256 == 0
+    assert step(hctx, shapes, ws=0) == B.MUON_ERR_WORKSPACE
+    assert step(hctx, shapes, ws=FAKE * 256 + 16) == B.MUON_ERR_WORKSPACE
+    assert step(hctx, shapes, wsb=need - 1) == B.MUON_ERR_WORKSPACE
+    assert step(hctx, shapes, wsb=need) == B.MUON_ERR_DEVICE
+
+
+def test_debug_gemm_validation(hctx):
+    f = B._lib.muon_debug_gemm
+    P = ctypes.c_void_p(FAKE)
+    assert f(hctx, 3, 1, 64, 64, 64, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 0, 1, 96, 64, 64, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 0, 1, 64, 64, 100, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 1, 1, 64, 64, 128, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 2, 1, 64, 64, 128, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_DEVICE
+
+
+# ---------------------------------------------------------------- dispatcher / FLOP model
+
+def plan(hctx, shapes, **kw):
+    hp = B.make_hparams(**kw)
+    raw = [(0, 0, 0, r, c) for r, c in shapes]
+    return [B.muon_plan_info(hctx, raw, hp, i) for i in range(len(shapes))]
+
+
+def test_plan_flops_match_oracle_model(hctx):
+    shapes = [(2560, 9728), (9728, 2560), (64, 256), (300, 70), (2048, 2048), (512, 3584)]
+    for segs in [(2, 2, 1), (2, 3), (1, 1, 1, 1, 1), (5,), (3, 1, 1)]:
+        for mode in ("plain", "gram"):
+            for (r, c), e in zip(shapes, plan(hctx, shapes, segments=segs, mode=mode)):
+                assert e.mode == B.MODES[mode]
+                assert e.dense_flops == pytest.approx(flop_model.dense_flops(r, c, mode, segs), rel=1e-12)
+                m, n = min(r, c), max(r, c)
+                assert (e.m, e.n, e.transposed) == (m, n, int(r > c))
+                # symmetric outputs computed once: SYRK m'^2 n', squares m'^3, apply 2 m'^2 n'
+                nl, ns = flop_model.product_counts(mode, segs)
+                assert e.kernel_flops == pytest.approx((nl // 2) * 3.0 * m * m * n + ns * 1.0 * m ** 3, rel=1e-12)
+
+
+def test_auto_dispatch_follows_flop_model(hctx):
+    shapes = [(2048, 2048), (8192, 2048), (2048, 8192), (3584, 3584), (512, 3584), (18944, 3584),
+              (64, 256), (100, 140), (100, 160), (2560, 9728)]
+    for (r, c), e in zip(shapes, plan(hctx, shapes)):
+        g = flop_model.dense_flops(r, c, "gram")
+        p = flop_model.dense_flops(r, c, "plain")
+        assert e.mode == (B.MUON_NS_GRAM if g < p else B.MUON_NS_PLAIN), (r, c)
+    es = plan(hctx, shapes)
+    assert es[0].mode == B.MUON_NS_PLAIN and es[1].mode == B.MUON_NS_GRAM and es[3].mode == B.MUON_NS_PLAIN
+    # the crossover sits at n'/m' = 1.5 for segments 2+2+1
+    assert es[7].mode == B.MUON_NS_PLAIN and es[8].mode == B.MUON_NS_GRAM
+
+
+def test_grouping_by_canonical_shape(hctx):
+    shapes = [(64, 256), (256, 64), (128, 512), (64, 256), (2048, 8192)]
+    es = plan(hctx, shapes)
+    assert es[0].group == es[1].group == es[3].group
+    assert len({es[0].group, es[2].group, es[4].group}) == 3
+    # largest work first
+    assert es[4].group == 0
+
+
+def test_workspace_size_is_deterministic_and_grows(hctx):
+    hp = B.make_hparams()
+    one = B.muon_workspace_size(hctx, [(0, 0, 0, 256, 1024)], hp)
+    two = B.muon_workspace_size(hctx, [(0, 0, 0, 256, 1024)] * 2, hp)
+    assert one == B.muon_workspace_size(hctx, [(0, 0, 0, 256, 1024)], hp)
+    assert two > one
+    f32 = B.muon_workspace_size(hctx, [(0, 0, 0, 256, 1024)], B.make_hparams(ns_dtype="f32"))
+    assert f32 > one

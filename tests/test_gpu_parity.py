@@ -1,0 +1,186 @@
+"""End-to-end parity of muon_step (through the C ABI) against the fp64 oracle.
+
+Compared quantities (the tolerances the method's precision allows):
+  * O, the orthogonalised update, recovered as (W - W') / lr in float64 (wd = 0), by
+    relative Frobenius error: <= 1e-4 on the fp32 path, <= 2e-2 on the bf16 path;
+  * M', the new momentum: exact to the storage rounding (fp32: 1e-6, bf16: 2^-8 relative
+    elementwise);
+  * W' itself: W' = W - lr*O within the same bound scaled by lr.
+Inputs come from the seeded generators both sides share; every GPU input value is exact
+in its storage dtype and read exactly by the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from matrix_orthogonalising_optimizer_muon_amd import workloads as wl  # noqa: E402
+from oracle import muon as om  # noqa: E402
+from tests.gpu_util import GpuState, rel, run_step, to_np  # noqa: E402
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def B():
+    from matrix_orthogonalising_optimizer_muon_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def ctx(B):
+    c = B.muon_init(0)
+    yield c
+    B.muon_destroy(c)
+
+
+def oracle_kwargs(w, hp_mode, segments, lr=None):
+    return dict(lr=w.lr if lr is None else lr, mu=w.mu, wd=w.wd, nesterov=True, eps=1e-7,
+                mode=hp_mode, segments=segments)
+
+
+def check_step(B, ctx, w, indices=None, mode="gram", segments=(2, 2, 1), steps=1, gpu_mode=None,
+               tol=None, mode_of=None):
+    """Run `steps` steps on the GPU and in the oracle from the same seeded state and
+    gradients; compare after each. The oracle carries its own float64 trajectory (its
+    inputs are only the generators' values, never GPU results)."""
+    tol = tol or TOL[w.ns_dtype]
+    st = GpuState(w, indices)
+    hp = B.make_hparams(lr=w.lr, momentum=w.mu, weight_decay=w.wd, segments=segments,
+                        mode=gpu_mode or mode, w_dtype=w.w_dtype, g_dtype=w.g_dtype,
+                        m_dtype=w.m_dtype, ns_dtype=w.ns_dtype)
+    W_o = [wl.weight_np(w, i).astype(np.float64) for i in st.indices]
+    M_o = [wl.momentum0_np(w, i).astype(np.float64) for i in st.indices]
+    worst = 0.0
+    for s in range(steps):
+        st.load_gradients(s)
+        W_prev = [to_np(x) for x in st.W]
+        run_step(ctx, st, hp)
+        for k, i in enumerate(st.indices):
+            G = wl.gradient_np(w, s, i).astype(np.float64)
+            m_k = mode_of(w.matrices[i]) if mode_of else mode
+            W_new, M_new, O_ref = om.muon_step(W_o[k], G, M_o[k], **oracle_kwargs(w, m_k, segments))
+            W_gpu, M_gpu = to_np(st.W[k]), to_np(st.M[k])
+            assert np.all(np.isfinite(W_gpu)) and np.all(np.isfinite(M_gpu))
+            O_gpu = (W_prev[k] - W_gpu) / w.lr
+            e = rel(O_gpu, O_ref)
+            worst = max(worst, e)
+            assert e <= tol, (w.name, i, s, e)
+            if s == 0:  # from M = 0 the new momentum is G itself: exact
+                assert np.array_equal(M_gpu, M_new), (w.name, i)
+            else:       # the stored momentum carries one storage rounding per step
+                u = 2.0 ** -24 if w.m_dtype == "f32" else 2.0 ** -8
+                assert rel(M_gpu, M_new) <= (s + 1) * u, (w.name, i, s)
+            W_o[k], M_o[k] = W_new, M_new
+    return worst
+
+
+# ---------------------------------------------------------------- fp32 path (1e-4)
+
+@pytest.mark.parametrize("mode", ["plain", "gram"])
+def test_fp32_single_256x1024(B, ctx, mode):
+    check_step(B, ctx, wl.WORKLOADS["single_fp32_256x1024"], mode=mode)
+
+
+@pytest.mark.parametrize("mode,segments", [("gram", (2, 3)), ("gram", (1, 1, 1, 1, 1)), ("gram", (5,)),
+                                           ("plain", (3,))])
+def test_fp32_schedules(B, ctx, mode, segments):
+    w = wl.custom("f32sched", [(96, 200)], dtype="f32", wid=201)
+    check_step(B, ctx, w, mode=mode, segments=segments)
+
+
+def test_fp32_ragged_and_tall(B, ctx):
+    w = wl.custom("f32ragged", [(100, 300), (300, 100), (130, 130), (1, 17), (65, 1000)], dtype="f32", wid=202)
+    check_step(B, ctx, w, mode="gram")
+    check_step(B, ctx, w, mode="plain")
+
+
+# ---------------------------------------------------------------- bf16 path (2e-2)
+
+@pytest.mark.parametrize("mode", ["plain", "gram"])
+def test_bf16_lowrank_small(B, ctx, mode):
+    w = wl.custom("bf16lr", [(256, 1024)], structure="lowrank", rank=16, wid=203)
+    check_step(B, ctx, w, mode=mode)
+
+
+def test_bf16_ragged_mixed_list(B, ctx):
+    shapes = [(100, 300), (300, 100), (130, 130), (1, 17), (65, 1000), (192, 640), (64, 256), (256, 64)]
+    w = wl.custom("bf16ragged", shapes, structure="gaussian", wid=204)
+    check_step(B, ctx, w, mode="gram")
+    check_step(B, ctx, w, mode="plain")
+
+
+def test_bf16_auto_dispatch_multi_step(B, ctx):
+    # decoder-like shapes (square -> plain, 4:1 -> Gram), momentum carried over 3 steps
+    shapes = [(256, 256), (1024, 256), (256, 1024), (256, 256)]
+    w = wl.custom("bf16dec", shapes, structure="lowrank", rank=8, wid=205, steps=3)
+    mode_of = lambda s: "gram" if max(s.rows, s.cols) / min(s.rows, s.cols) > 1.5 else "plain"
+    check_step(B, ctx, w, mode="gram", gpu_mode="auto", steps=3, mode_of=mode_of)
+
+
+def test_bf16_weight_update_bf16_weights(B, ctx):
+    w = wl.custom("bf16w", [(128, 384)], structure="gaussian", wid=206)
+    w = wl.Workload(**{**w.__dict__, "w_dtype": "bf16"})
+    st = GpuState(w)
+    st.load_gradients(0)
+    hp = B.make_hparams(w_dtype="bf16", mode="gram")
+    W0 = to_np(st.W[0])
+    run_step(ctx, st, hp)
+    W_ref, _, _ = om.muon_step(W0, to_np(st.G[0]), np.zeros_like(W0), mode="gram")
+    # bf16 storage of W' dominates: elementwise within one bf16 rounding plus lr*2e-2
+    assert np.all(np.abs(to_np(st.W[0]) - W_ref) <= 2.0 ** -8 * np.abs(W_ref) + 0.02 * 0.02 * np.abs(W_ref - W0).max())
+
+
+def test_bf16_2560x9728_full_size(B, ctx):
+    """The 2560 x 9728 bf16 momentum matrix at full size, Gram 2+2+1 and plain."""
+    w = wl.WORKLOADS["single_bf16_2560x9728"]
+    e_gram = check_step(B, ctx, w, mode="gram")
+    e_plain = check_step(B, ctx, w, mode="plain")
+    assert e_gram <= 2e-2 and e_plain <= 2e-2
+
+
+def test_small_batch_832_full(B, ctx):
+    w = wl.WORKLOADS["small_batch_832"]
+    check_step(B, ctx, w, mode="gram", gpu_mode="auto")
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_zero_gradient_and_determinism(B, ctx):
+    w = wl.custom("zero", [(64, 256), (300, 70)], structure="gaussian", wid=207)
+    st = GpuState(w)
+    st.G = [torch.zeros_like(m) for m in st.M]
+    hp = B.make_hparams(weight_decay=0.1, mode="gram")
+    W0 = [to_np(x) for x in st.W]
+    run_step(ctx, st, hp)
+    for k in range(2):
+        Wn = to_np(st.W[k])
+        assert np.all(np.isfinite(Wn))
+        assert np.allclose(Wn, W0[k] * (1 - 0.02 * 0.1), rtol=1e-6, atol=0)
+    # identical inputs -> bitwise identical outputs (fixed-order reductions)
+    outs = []
+    for _ in range(2):
+        st2 = GpuState(wl.custom("det", [(192, 640), (640, 192)], structure="lowrank", rank=4, wid=208))
+        st2.load_gradients(0)
+        run_step(ctx, st2, B.make_hparams())
+        outs.append([x.clone() for x in st2.W + st2.M])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_error_leaves_state_untouched(B, ctx):
+    w = wl.custom("err", [(64, 256)], structure="gaussian", wid=209)
+    st = GpuState(w)
+    st.load_gradients(0)
+    W0, M0 = st.W[0].clone(), st.M[0].clone()
+    mats = st.triples()
+    hp = B.make_hparams()
+    nbytes = B.muon_workspace_size(ctx, mats, hp)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    assert B.muon_step(ctx, mats, hp, ws.data_ptr(), nbytes - 256) == B.MUON_ERR_WORKSPACE
+    bad = B.make_hparams(momentum=1.5)
+    assert B.muon_step(ctx, mats, bad, ws.data_ptr(), nbytes) == B.MUON_ERR_ARG
+    torch.cuda.synchronize()
+    assert torch.equal(st.W[0], W0) and torch.equal(st.M[0], M0)

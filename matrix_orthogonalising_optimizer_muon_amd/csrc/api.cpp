@@ -592,6 +592,7 @@ int muon_debug_gemm(muon_ctx* ctx, int kind, int ns_dtype, int tile, int64_t M, 
                     const void* A, const void* B, const void* E, void* C, float alpha, float beta,
                     float gamma, float bscale, void* stream) {
   try {
+    if (kind == 0 && !B) B = A;  // X X^T: the second operand is X itself
     if (!ctx || !A || !B || !C) return MUON_ERR_ARG;
     if (kind < 0 || kind > 2 || (ns_dtype != MUON_F32 && ns_dtype != MUON_BF16)) return MUON_ERR_ARG;
     if (tile != 64 && tile != 128) return MUON_ERR_ARG;

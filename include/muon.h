@@ -103,7 +103,7 @@ typedef struct muon_plan_entry {
   int32_t transposed;    /* 1 if rows > cols (processed as the transpose) */
   int64_t m, n;          /* canonical short side m' and long side n' */
   int32_t group;         /* same-shape group index (one batched launch per stage) */
-  int32_t tile;          /* tile edge of the GEMM kernels used (64 or 128) */
+  int32_t tile;          /* tile rows of the apply GEMM kernel used (64, 128 or 256) */
   double dense_flops;    /* matmul FLOPs as the MuonX article counts them (2m'^2n', 2m'^3) */
   double kernel_flops;   /* FLOPs the kernels actually perform (symmetric outputs halved) */
 } muon_plan_entry;
@@ -159,7 +159,9 @@ int muon_plan_info(muon_ctx *ctx, const muon_matrix *mats, int count,
  * tiles mirrored; 1 = symmetric-output square product A B^T with epilogue
  * alpha*acc + beta*E + gamma*I (fp16 or fp32); 2 = apply C = alpha*A*(bscale*B) + beta*E
  * with B (K x N row-major, bf16 converted to fp16, or fp32) and C in B's dtype.
- * ns_dtype selects the bf16/fp16 or the fp32 kernels; tile is 64 or 128. Buffers are
+ * ns_dtype selects the bf16/fp16 or the fp32 kernels; tile selects the workgroup tile:
+ * 0 = 64x64, 1 = 128x128, 2 = 256x128 (kind 2 only), 3 = 256x256 (not fp32); an
+ * unavailable combination returns MUON_ERR_UNSUPPORTED. Buffers are
  * dense row-major with leading dimension equal to their column count; M, N, K must be
  * multiples of 64. */
 int muon_debug_gemm(muon_ctx *ctx, int kind, int ns_dtype, int tile, int64_t M, int64_t N,

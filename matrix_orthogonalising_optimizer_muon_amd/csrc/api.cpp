@@ -59,7 +59,7 @@ struct Group {
   int64_t m = 0, n = 0;        // canonical m' <= n'
   int64_t Mp = 0, Np = 0;      // padded
   int mode = MUON_NS_GRAM;
-  int tile_sq = 64, tile_ap = 64;
+  int tile_sq = TILE_64, tile_ap = TILE_64;  // TileCfg of the symmetric / apply stages
   std::vector<int> members;    // indices into the caller's list
   int table_base = 0;          // first descriptor of this group in the table
   // workspace offsets (bytes) and per-matrix element strides
@@ -143,9 +143,10 @@ int choose_mode(int64_t m, int64_t n, const muon_hparams& hp) {
                                                                                       : MUON_NS_PLAIN;
 }
 
-// Tile edge: 128 when the batch still gives every CU a couple of tiles, else 64.
+// Tile configuration: 128 x 128 when the batch still gives every CU a couple of tiles,
+// else 64 x 64.
 int choose_tile(int64_t tiles128, int64_t count, int cu) {
-  return (tiles128 * count >= 2LL * cu) ? 128 : 64;
+  return (tiles128 * count >= 2LL * cu) ? TILE_128 : TILE_64;
 }
 
 int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams& hp,
@@ -274,7 +275,8 @@ GemmParams base_params(const Group& g, const StepEnv& env) {
   return p;
 }
 
-void set_sym_tiles(GemmParams& p, int64_t Mp, int tile) {
+void set_sym_tiles(GemmParams& p, int64_t Mp, int cfg) {
+  const int tile = tile_bm(cfg);
   const int nt = static_cast<int>((Mp + tile - 1) / tile);
   p.tiles_m = p.tiles_n = nt;
   p.tiles = nt * (nt + 1) / 2;
@@ -324,8 +326,8 @@ hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* 
   p.alpha = alpha; p.bscale = bscale; p.bscale_spow = bspow;
   p.beta = beta; p.beta_spow = beta_spow;
   const int t = g.tile_ap;
-  p.tiles_m = static_cast<int32_t>((g.Mp + t - 1) / t);
-  p.tiles_n = static_cast<int32_t>((g.Np + t - 1) / t);
+  p.tiles_m = static_cast<int32_t>((g.Mp + tile_bm(t) - 1) / tile_bm(t));
+  p.tiles_n = static_cast<int32_t>((g.Np + tile_bn(t) - 1) / tile_bn(t));
   p.tiles = p.tiles_m * p.tiles_n;
   if (update) {
     p.table = table;
@@ -579,7 +581,7 @@ int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon
     out->m = g.m;
     out->n = g.n;
     out->group = plan.group_of[index];
-    out->tile = g.tile_ap;
+    out->tile = tile_bm(g.tile_ap);
     out->dense_flops = dense_flops(g.m, g.n, g.mode, *hp);
     out->kernel_flops = kernel_flops(g.m, g.n, g.mode, *hp);
     return MUON_OK;
@@ -595,11 +597,11 @@ int muon_debug_gemm(muon_ctx* ctx, int kind, int ns_dtype, int tile, int64_t M, 
     if (kind == 0 && !B) B = A;  // X X^T: the second operand is X itself
     if (!ctx || !A || !B || !C) return MUON_ERR_ARG;
     if (kind < 0 || kind > 2 || (ns_dtype != MUON_F32 && ns_dtype != MUON_BF16)) return MUON_ERR_ARG;
-    if (tile != 64 && tile != 128) return MUON_ERR_ARG;
+    if (tile < 0 || tile >= TILE_COUNT) return MUON_ERR_ARG;
     if (M < 64 || N < 64 || K < 64 || M % 64 || N % 64 || K % 64 || M > kMaxDim || N > kMaxDim ||
         K > kMaxDim)
       return MUON_ERR_ARG;
-    if ((kind == 0 || kind == 1) && M != N) return MUON_ERR_ARG;
+    if ((kind == 0 || kind == 1) && (M != N || tile_bm(tile) != tile_bn(tile))) return MUON_ERR_ARG;
     if (ctx->device < 0) return MUON_ERR_DEVICE;
     DeviceGuard dg(ctx->device);
     if (!dg.ok) return MUON_ERR_HIP;
@@ -614,19 +616,20 @@ int muon_debug_gemm(muon_ctx* ctx, int kind, int ns_dtype, int tile, int64_t M, 
     if (kind == 2) {
       op = OP_APPLY;
       p.lda = K; p.ldb = N; p.ldc = N; p.lde = N;
-      p.tiles_m = static_cast<int32_t>((M + tile - 1) / tile);
-      p.tiles_n = static_cast<int32_t>((N + tile - 1) / tile);
+      p.tiles_m = static_cast<int32_t>((M + tile_bm(tile) - 1) / tile_bm(tile));
+      p.tiles_n = static_cast<int32_t>((N + tile_bn(tile) - 1) / tile_bn(tile));
       p.tiles = p.tiles_m * p.tiles_n;
     } else {
       op = kind == 0 ? OP_SYRK : OP_SQUARE;
       if (kind == 0) B = A, p.B = A;
       p.lda = K; p.ldb = K; p.ldc = N; p.lde = N;
-      const int nt = static_cast<int>((M + tile - 1) / tile);
+      const int nt = static_cast<int>((M + tile_bm(tile) - 1) / tile_bm(tile));
       p.tiles_m = p.tiles_n = nt;
       p.tiles = nt * (nt + 1) / 2;
     }
-    if (launch_gemm(op, ns_dtype == MUON_F32, tile, p, static_cast<hipStream_t>(stream)) != hipSuccess)
-      return MUON_ERR_HIP;
+    const hipError_t le = launch_gemm(op, ns_dtype == MUON_F32, tile, p, static_cast<hipStream_t>(stream));
+    if (le == hipErrorInvalidValue) return MUON_ERR_UNSUPPORTED;
+    if (le != hipSuccess) return MUON_ERR_HIP;
     return MUON_OK;
   } catch (...) {
     return MUON_ERR_HIP;

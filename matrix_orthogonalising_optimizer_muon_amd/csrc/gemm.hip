@@ -16,17 +16,19 @@
 // are 8 chunks of 16 bytes, XOR-swizzled per row so that both the fragment reads (32
 // consecutive rows, same chunk) and the transposed NN writes (rows 8 apart) spread over
 // all banks.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace muon {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
 constexpr int kChunks = 8;  // 16-byte chunks per 128-byte LDS row
 
 __device__ __forceinline__ int swz(int row, int chunk) {
@@ -124,19 +126,22 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, bool NN, bool SYM, int EPI, typename TC>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
-  static_assert(WM * WN == 4, "4 waves");
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmParams p) {
+  constexpr int NT = 64 * WM * WN;                     // threads
   constexpr int ES = (KIND == KIND_F32) ? 4 : 2;      // element bytes in LDS / MFMA
-  constexpr int VEC = 16 / ES;                         // elements per chunk
-  constexpr int BK = kChunks * VEC;                    // k per LDS slice
+  constexpr int VEC = 16 / ES;                         // elements per 16-byte chunk
+  constexpr int BK = kChunks * VEC;                    // k per LDS slice (128 bytes)
   constexpr int TWM = BM / WM, TWN = BN / WN;          // wave tile
-  constexpr int FM = TWM / 32, FN = TWN / 32;          // MFMA blocks per wave
+  constexpr int FM = TWM / 32, FN = TWN / 32;          // 32x32 MFMA blocks per wave
   static_assert(FM >= 1 && FN >= 1, "wave tile");
-  constexpr int A_CH = BM * kChunks / kThreads;        // A chunks per thread
-  static_assert(A_CH * kThreads == BM * kChunks, "A split");
-  constexpr int B_CH = BN * kChunks / kThreads;        // NT B chunks per thread
-  constexpr int B_BLOCKS = (BK / VEC) * (BN / VEC);    // NN: VEC x VEC blocks
-  constexpr int B_BLK = (B_BLOCKS + kThreads - 1) / kThreads;
+  constexpr int A_CH = (BM * kChunks + NT - 1) / NT;   // A chunks per thread
+  constexpr int B_CH = (BN * kChunks + NT - 1) / NT;   // NT B chunks per thread
+  // NN: the BK x BN slice of row-major B is cut into half-blocks of VEC/2 k-rows by VEC
+  // n-columns; each is transposed in registers into VEC 8-byte k-runs.
+  constexpr int HR = VEC / 2;
+  constexpr int N_HB = (BK / HR) * (BN / VEC);
+  constexpr int HB_T = (N_HB + NT - 1) / NT;
+  constexpr int KSTEPS = kChunks / 2;                  // MFMA k-steps per slice
 
   __shared__ u32x4 lds[2][(BM + BN) * kChunks];
 
@@ -155,52 +160,51 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 
   const float bscale = scaled(p.bscale, p.s, mat, p.bscale_spow);
 
+  // Global offsets (bytes, without k) of the chunks this thread stages. Rows past M or N
+  // are clamped to the last valid row: they only feed output rows/columns that are never
+  // stored, so the loads need no branches.
+  int64_t a_off[A_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = min(tid + i * NT, BM * kChunks - 1);
+    const int gr = min(m0 + c / kChunks, p.M - 1);
+    a_off[i] = (static_cast<int64_t>(gr) * p.lda + (c % kChunks) * VEC) * ES;
+  }
+  int64_t b_off[NN ? HB_T : B_CH];
+  if constexpr (!NN) {
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = min(tid + i * NT, BN * kChunks - 1);
+      const int gr = min(n0 + c / kChunks, p.N - 1);
+      b_off[i] = (static_cast<int64_t>(gr) * p.ldb + (c % kChunks) * VEC) * ES;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < HB_T; ++i) {
+      const int hb = min(tid + i * NT, N_HB - 1);
+      const int nb = hb % (BN / VEC), hk = hb / (BN / VEC);
+      const int gn = min(n0 + nb * VEC, p.N - VEC);
+      b_off[i] = (static_cast<int64_t>(hk * HR) * p.ldb + gn) * ES;
+    }
+  }
+
   u32x4 ra[A_CH];
-  u32x4 rbt[NN ? 1 : B_CH];
-  u32x4 rbn[NN ? B_BLK : 1][NN ? VEC : 1];
+  u32x4 rb[NN ? HB_T * HR : B_CH];
 
   auto load_global = [&](int k0) {
+    const int64_t ka = static_cast<int64_t>(k0) * ES;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / kChunks, kc = c % kChunks;
-      const int gr = m0 + row;
-      if (gr < p.M) {
-        ra[i] = *reinterpret_cast<const u32x4*>(Ab + (static_cast<int64_t>(gr) * p.lda + k0 + kc * VEC) * ES);
-      } else {
-        ra[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(Ab + a_off[i] + ka);
     if constexpr (!NN) {
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * kThreads;
-        const int row = c / kChunks, kc = c % kChunks;
-        const int gr = n0 + row;
-        if (gr < p.N) {
-          rbt[i] = *reinterpret_cast<const u32x4*>(Bb + (static_cast<int64_t>(gr) * p.ldb + k0 + kc * VEC) * ES);
-        } else {
-          rbt[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
+      for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i] + ka);
     } else {
+      const int64_t kb = static_cast<int64_t>(k0) * p.ldb * ES;
 #pragma unroll
-      for (int i = 0; i < B_BLK; ++i) {
-        const int b = tid + i * kThreads;
-        if (B_BLOCKS % kThreads == 0 || b < B_BLOCKS) {
-          const int kb = b / (BN / VEC), nb = b % (BN / VEC);
-          const int gn = n0 + nb * VEC;
+      for (int i = 0; i < HB_T; ++i)
 #pragma unroll
-          for (int r = 0; r < VEC; ++r) {
-            const int gk = k0 + kb * VEC + r;
-            if (gn < p.N) {
-              rbn[i][r] = *reinterpret_cast<const u32x4*>(Bb + (static_cast<int64_t>(gk) * p.ldb + gn) * ES);
-            } else {
-              rbn[i][r] = u32x4{0u, 0u, 0u, 0u};
-            }
-          }
-        }
-      }
+        for (int r = 0; r < HR; ++r)
+          rb[i * HR + r] = *reinterpret_cast<const u32x4*>(Bb + b_off[i] + kb + static_cast<int64_t>(r) * p.ldb * ES);
     }
   };
 
@@ -209,54 +213,54 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     u32x4* lb = lds[stage] + BM * kChunks;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * kThreads;
-      la[swz(c / kChunks, c % kChunks)] = ra[i];
+      const int c = tid + i * NT;
+      if ((BM * kChunks) % NT == 0 || c < BM * kChunks) la[swz(c / kChunks, c % kChunks)] = ra[i];
     }
     if constexpr (!NN) {
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * kThreads;
-        lb[swz(c / kChunks, c % kChunks)] = rbt[i];
+        const int c = tid + i * NT;
+        if ((BN * kChunks) % NT == 0 || c < BN * kChunks) lb[swz(c / kChunks, c % kChunks)] = rb[i];
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < B_BLK; ++i) {
-        const int b = tid + i * kThreads;
-        if (B_BLOCKS % kThreads == 0 || b < B_BLOCKS) {
-          const int kb = b / (BN / VEC), nb = b % (BN / VEC);
-          if constexpr (KIND == KIND_F16) {
-            // bf16 rows -> scaled fp16 rows, then an 8x8 transpose.
-            u32x4 cv[8], tr[8];
+      for (int i = 0; i < HB_T; ++i) {
+        const int hb = tid + i * NT;
+        if (N_HB % NT != 0 && hb >= N_HB) continue;
+        const int nb = hb % (BN / VEC), hk = hb / (BN / VEC);
+        const int kb = hk >> 1, half = hk & 1;
+        if constexpr (KIND == KIND_F16) {
+          // 4 bf16 rows of 8 -> scaled fp16, then 8 columns of 4 k-values.
+          unsigned int w[4][4];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              unsigned int w[4];
+          for (int r = 0; r < 4; ++r)
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const unsigned int x = rbn[i][r][q];
-                const float lo = __uint_as_float(x << 16) * bscale;
-                const float hi = __uint_as_float(x & 0xFFFF0000u) * bscale;
-                w[q] = static_cast<unsigned int>(f32_to_f16(lo)) |
-                       (static_cast<unsigned int>(f32_to_f16(hi)) << 16);
-              }
-              cv[r] = u32x4{w[0], w[1], w[2], w[3]};
+            for (int q = 0; q < 4; ++q) {
+              const unsigned int x = rb[i * HR + r][q];
+              const float lo = __uint_as_float(x << 16) * bscale;
+              const float hi = __uint_as_float(x & 0xFFFF0000u) * bscale;
+              w[r][q] = static_cast<unsigned int>(f32_to_f16(lo)) |
+                        (static_cast<unsigned int>(f32_to_f16(hi)) << 16);
             }
-            transpose8x8_16(cv, tr);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) lb[swz(nb * 8 + j, kb)] = tr[j];
-          } else {
-            static_assert(KIND == KIND_F32, "NN operand kinds");
-            u32x4 cv[4], tr[4];
+          for (int q = 0; q < 4; ++q) {
+            // columns 2q (low halves) and 2q+1 (high halves) of the 4 rows
+            const u32x2 lo{__builtin_amdgcn_perm(w[1][q], w[0][q], 0x05040100u),
+                           __builtin_amdgcn_perm(w[3][q], w[2][q], 0x05040100u)};
+            const u32x2 hi{__builtin_amdgcn_perm(w[1][q], w[0][q], 0x07060302u),
+                           __builtin_amdgcn_perm(w[3][q], w[2][q], 0x07060302u)};
+            reinterpret_cast<u32x2*>(&lb[swz(nb * 8 + 2 * q, kb)])[half] = lo;
+            reinterpret_cast<u32x2*>(&lb[swz(nb * 8 + 2 * q + 1, kb)])[half] = hi;
+          }
+        } else {
+          static_assert(KIND == KIND_F32, "NN operand kinds");
+          // 2 fp32 rows of 4 -> 4 columns of 2 k-values.
+          const u32x4 x0 = rb[i * HR], x1 = rb[i * HR + 1];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const u32x4 x = rbn[i][r];
-              cv[r] = u32x4{__float_as_uint(__uint_as_float(x.x) * bscale),
-                            __float_as_uint(__uint_as_float(x.y) * bscale),
-                            __float_as_uint(__uint_as_float(x.z) * bscale),
-                            __float_as_uint(__uint_as_float(x.w) * bscale)};
-            }
-            transpose4x4_32(cv, tr);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) lb[swz(nb * 4 + j, kb)] = tr[j];
+          for (int j = 0; j < 4; ++j) {
+            const u32x2 v{__float_as_uint(__uint_as_float(x0[j]) * bscale),
+                          __float_as_uint(__uint_as_float(x1[j]) * bscale)};
+            reinterpret_cast<u32x2*>(&lb[swz(nb * 4 + j, kb)])[half] = v;
           }
         }
       }
@@ -275,31 +279,43 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   const int wn0 = (wave % WN) * TWN;
   const int nk = p.K / BK;
 
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
+  u32x4 fa[2][FM], fb[2][FN];
+  auto load_frags = [&](int buf, const u32x4* la, const u32x4* lb, int kk) {
+    const int ch = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[buf][i] = la[swz(wm0 + i * 32 + (lane & 31), ch)];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[buf][j] = lb[swz(wn0 + j * 32 + (lane & 31), ch)];
+  };
 
-  for (int kt = 0; kt < nk; ++kt) {
+  // One 128-byte slice of K: fragments double-buffered across the k-steps; the staged
+  // next slice goes to the other LDS buffer half-way through.
+  auto slice = [&](int kt, auto has_next_tag) {
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     const int stage = kt & 1;
-    if (kt + 1 < nk) load_global((kt + 1) * BK);
     const u32x4* la = lds[stage];
     const u32x4* lb = lds[stage] + BM * kChunks;
+    if constexpr (HAS_NEXT) load_global((kt + 1) * BK);
+    load_frags(0, la, lb, 0);
 #pragma unroll
-    for (int kk = 0; kk < kChunks / 2; ++kk) {
-      const int ch = 2 * kk + (lane >> 5);
-      u32x4 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = la[swz(wm0 + i * 32 + (lane & 31), ch)];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = lb[swz(wn0 + j * 32 + (lane & 31), ch)];
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (kk + 1 < KSTEPS) load_frags((kk + 1) & 1, la, lb, kk + 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) mma<KIND>(acc[i][j], af[i], bfr[j]);
+        for (int j = 0; j < FN; ++j) mma<KIND>(acc[i][j], fa[kk & 1][i], fb[kk & 1][j]);
+      if constexpr (HAS_NEXT) {
+        if (kk == KSTEPS / 2 - 1) store_lds(stage ^ 1);
+      }
     }
-    if (kt + 1 < nk) store_lds(stage ^ 1);
     __syncthreads();
-  }
+  };
+
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+  for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, std::true_type{});
+  slice(nk - 1, std::false_type{});
 
   // ---- epilogue ----
   const float alpha = scaled(p.alpha, p.s, mat, p.alpha_spow);
@@ -336,8 +352,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
             const int64_t ei = static_cast<int64_t>(r) * p.lde + c;
             if constexpr (sizeof(TC) == 4) {
               v += beta * reinterpret_cast<const float*>(E)[ei];
-            } else if constexpr (KIND == KIND_F32) {
-              v += 0.0f;  // not instantiated
             } else {
               const unsigned short h = reinterpret_cast<const unsigned short*>(E)[ei];
               v += beta * ((EPI == EPI_UPDATE || !SYM) ? bf16_to_f32(h) : f16_to_f32(h));
@@ -374,40 +388,45 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   }
 }
 
-template <int KIND, int T, bool NN, bool SYM, int EPI, typename TC>
-hipError_t launch_cfg(const GemmParams& p, hipStream_t st) {
-  dim3 grid(p.tiles, p.count);
-  if (T == 128) {
-    hipLaunchKernelGGL((gemm_kernel<KIND, 128, 128, 2, 2, NN, SYM, EPI, TC>), grid, dim3(kThreads), 0, st, p);
-  } else {
-    hipLaunchKernelGGL((gemm_kernel<KIND, 64, 64, 2, 2, NN, SYM, EPI, TC>), grid, dim3(kThreads), 0, st, p);
-  }
+template <int KIND, int BM, int BN, int WM, int WN, bool NN, bool SYM, int EPI, typename TC>
+hipError_t launch_shape(const GemmParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, NN, SYM, EPI, TC>), dim3(p.tiles, p.count),
+                     dim3(64 * WM * WN), 0, st, p);
   return hipGetLastError();
 }
 
 template <int KIND, bool NN, bool SYM, int EPI, typename TC>
-hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t st) {
-  if (tile == 128) return launch_cfg<KIND, 128, NN, SYM, EPI, TC>(p, st);
-  return launch_cfg<KIND, 64, NN, SYM, EPI, TC>(p, st);
+hipError_t launch_tile(int cfg, const GemmParams& p, hipStream_t st) {
+  switch (cfg) {
+    case TILE_64: return launch_shape<KIND, 64, 64, 2, 2, NN, SYM, EPI, TC>(p, st);
+    case TILE_128: return launch_shape<KIND, 128, 128, 2, 2, NN, SYM, EPI, TC>(p, st);
+    case TILE_256:  // 8 waves (2 per SIMD), wave tile 128 x 64
+      if constexpr (KIND != KIND_F32) return launch_shape<KIND, 256, 256, 2, 4, NN, SYM, EPI, TC>(p, st);
+      return hipErrorInvalidValue;
+    case TILE_256x128:  // 8 waves, wave tile 64 x 64
+      if constexpr (!SYM && KIND != KIND_F32) return launch_shape<KIND, 256, 128, 4, 2, NN, SYM, EPI, TC>(p, st);
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gemm(GemmOp op, bool ns_f32, int tile, const GemmParams& p, hipStream_t st) {
+hipError_t launch_gemm(GemmOp op, bool ns_f32, int cfg, const GemmParams& p, hipStream_t st) {
   if (p.tiles <= 0 || p.count <= 0) return hipSuccess;
   if (ns_f32) {
     switch (op) {
       case OP_SYRK:
-      case OP_SQUARE: return launch_tile<KIND_F32, false, true, EPI_STORE, float>(tile, p, st);
-      case OP_APPLY: return launch_tile<KIND_F32, true, false, EPI_STORE, float>(tile, p, st);
-      case OP_UPDATE: return launch_tile<KIND_F32, true, false, EPI_UPDATE, float>(tile, p, st);
+      case OP_SQUARE: return launch_tile<KIND_F32, false, true, EPI_STORE, float>(cfg, p, st);
+      case OP_APPLY: return launch_tile<KIND_F32, true, false, EPI_STORE, float>(cfg, p, st);
+      case OP_UPDATE: return launch_tile<KIND_F32, true, false, EPI_UPDATE, float>(cfg, p, st);
     }
   } else {
     switch (op) {
-      case OP_SYRK: return launch_tile<KIND_BF16, false, true, EPI_STORE, unsigned short>(tile, p, st);
-      case OP_SQUARE: return launch_tile<KIND_F16, false, true, EPI_STORE, unsigned short>(tile, p, st);
-      case OP_APPLY: return launch_tile<KIND_F16, true, false, EPI_STORE, unsigned short>(tile, p, st);
-      case OP_UPDATE: return launch_tile<KIND_F16, true, false, EPI_UPDATE, unsigned short>(tile, p, st);
+      case OP_SYRK: return launch_tile<KIND_BF16, false, true, EPI_STORE, unsigned short>(cfg, p, st);
+      case OP_SQUARE: return launch_tile<KIND_F16, false, true, EPI_STORE, unsigned short>(cfg, p, st);
+      case OP_APPLY: return launch_tile<KIND_F16, true, false, EPI_STORE, unsigned short>(cfg, p, st);
+      case OP_UPDATE: return launch_tile<KIND_F16, true, false, EPI_UPDATE, unsigned short>(cfg, p, st);
     }
   }
   return hipErrorInvalidValue;

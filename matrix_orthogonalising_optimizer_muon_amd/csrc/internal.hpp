@@ -54,8 +54,19 @@ enum GemmOp : int {
   OP_UPDATE = 3,   // as OP_APPLY, epilogue updates W
 };
 
+// Workgroup tile configurations (4 waves each). Symmetric-output stages need BM == BN.
+enum TileCfg : int {
+  TILE_64 = 0,       // 64 x 64, wave tile 32 x 32
+  TILE_128 = 1,      // 128 x 128, wave tile 64 x 64
+  TILE_256x128 = 2,  // 256 x 128, wave tile 128 x 64
+  TILE_256 = 3,      // 256 x 256, wave tile 128 x 128
+  TILE_COUNT = 4
+};
+inline int tile_bm(int cfg) { return cfg == TILE_64 ? 64 : cfg == TILE_128 ? 128 : 256; }
+inline int tile_bn(int cfg) { return cfg == TILE_64 ? 64 : cfg == TILE_256 ? 256 : 128; }
+
 // Launch one batched GEMM stage. ns_f32: fp32 kernels, else bf16/fp16 kernels.
-hipError_t launch_gemm(GemmOp op, bool ns_f32, int tile, const GemmParams& p, hipStream_t st);
+hipError_t launch_gemm(GemmOp op, bool ns_f32, int cfg, const GemmParams& p, hipStream_t st);
 
 // Momentum + canonical-orientation write of U + per-block partial sums of U^2.
 struct MomentumParams {

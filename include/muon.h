@@ -110,8 +110,8 @@ typedef struct muon_plan_entry {
 
 /* Aggregated launch timings of one stage kind and shape (muon_profile_read). */
 typedef struct muon_profile_entry {
-  char stage[32];        /* "table", "momentum", "norm_finalize", "syrk", "square",
-                            "apply", "apply_update" */
+  char stage[32];        /* "table", "momentum", "norm_finalize", "transpose", "syrk",
+                            "square", "apply", "apply_update" */
   int64_t m, n;          /* canonical shape of the group the launches served */
   int32_t count;         /* matrices per launch */
   int32_t launches;      /* launches aggregated */
@@ -154,19 +154,21 @@ int muon_step(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hpar
 int muon_plan_info(muon_ctx *ctx, const muon_matrix *mats, int count,
                    const muon_hparams *hp, int index, muon_plan_entry *out);
 
-/* Test-only entry point: one GEMM stage of the pipeline on caller buffers, synchronously
- * enqueued on `stream`. kind: 0 = symmetric X X^T (bf16 in, fp16 out; or fp32), upper
- * tiles mirrored; 1 = symmetric-output square product A B^T with epilogue
- * alpha*acc + beta*E + gamma*I (fp16 or fp32); 2 = apply C = alpha*A*(bscale*B) + beta*E
- * with B (K x N row-major, bf16 converted to fp16, or fp32) and C in B's dtype.
- * ns_dtype selects the bf16/fp16 or the fp32 kernels; tile selects the workgroup tile:
- * 0 = 64x64, 1 = 128x128, 2 = 256x128 (kind 2 only), 3 = 256x256 (not fp32); an
- * unavailable combination returns MUON_ERR_UNSUPPORTED. Buffers are
- * dense row-major with leading dimension equal to their column count; M, N, K must be
- * multiples of 64. */
+/* Test-only entry point: one GEMM stage of the pipeline on caller buffers, enqueued on
+ * `stream`. All products are A B^T with A (M x K) and B (N x K) row-major:
+ *   kind 0: C = alpha * A A^T, symmetric (upper tiles computed, mirrored); A is bf16 with
+ *           C fp16 (ns_dtype MUON_BF16) or both fp32 (MUON_F32); B is ignored.
+ *   kind 1: C = alpha * A B^T + beta * E + gamma * I with symmetric output; A, B, E, C
+ *           fp16 (MUON_BF16) or fp32; E (M x N) may be null.
+ *   kind 2: v = alpha * A B^T + beta * E^T with E stored N x M (may be null);
+ *           C (M x N) = oscale * v and, if C2 is not null, C2 (N x M) = oscale * v^T;
+ *           operands and outputs fp16 (MUON_BF16) or fp32.
+ * tile selects the workgroup tile: 0 = 64x64, 1 = 128x128, 2 = 256x128 (kind 2 only),
+ * 3 = 256x256 (not fp32); an unavailable combination returns MUON_ERR_UNSUPPORTED.
+ * Leading dimensions equal the column counts; M, N, K must be multiples of 64. */
 int muon_debug_gemm(muon_ctx *ctx, int kind, int ns_dtype, int tile, int64_t M, int64_t N,
-                    int64_t K, const void *A, const void *B, const void *E, void *C,
-                    float alpha, float beta, float gamma, float bscale, void *stream);
+                    int64_t K, const void *A, const void *B, const void *E, void *C, void *C2,
+                    float alpha, float beta, float gamma, float oscale, void *stream);
 
 /* Profiler read-out for a context created with MUON_FLAG_PROFILE: waits for the last
  * recorded launch, aggregates all launches recorded since the previous read by (stage,

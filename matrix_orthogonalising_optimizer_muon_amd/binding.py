@@ -91,7 +91,7 @@ _lib.muon_plan_info.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int,
                                 ctypes.POINTER(muon_plan_entry)]
 _lib.muon_plan_info.restype = ctypes.c_int
 _lib.muon_debug_gemm.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
-                                 ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, ctypes.c_float,
+                                 ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_float,
                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, _P]
 _lib.muon_debug_gemm.restype = ctypes.c_int
 _lib.muon_profile_read.argtypes = [_P, ctypes.POINTER(muon_profile_entry), ctypes.c_int,
@@ -201,13 +201,13 @@ def muon_plan_info(ctx, mats, hp: muon_hparams, index: int) -> muon_plan_entry:
     return out
 
 
-def muon_debug_gemm(ctx, kind, ns_dtype, tile, M, N, K, A, B, E, C, alpha=1.0, beta=0.0,
-                    gamma=0.0, bscale=1.0, stream_ptr=None) -> int:
+def muon_debug_gemm(ctx, kind, ns_dtype, tile, M, N, K, A, B, E, C, C2=None, alpha=1.0,
+                    beta=0.0, gamma=0.0, oscale=1.0, stream_ptr=None) -> int:
     if stream_ptr is None:
         stream_ptr = torch.cuda.current_stream().cuda_stream
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     return _lib.muon_debug_gemm(ctx, int(kind), DTYPES.get(ns_dtype, ns_dtype), int(tile), M, N, K,
-                                ptr(A), ptr(B), ptr(E), ptr(C), alpha, beta, gamma, bscale,
+                                ptr(A), ptr(B), ptr(E), ptr(C), ptr(C2), alpha, beta, gamma, oscale,
                                 ctypes.c_void_p(stream_ptr))
 
 

@@ -63,7 +63,9 @@ struct Group {
   std::vector<int> members;    // indices into the caller's list
   int table_base = 0;          // first descriptor of this group in the table
   // workspace offsets (bytes) and per-matrix element strides
-  size_t off_partials = 0, off_s = 0, off_x[2] = {0, 0}, off_sq[4] = {0, 0, 0, 0};
+  // X: canonical m' x n' iterate (first the momentum output U); XT[2]: its transposed
+  // copies (ping-pong); SQ: m' x m' buffers of the Gram-space recurrence.
+  size_t off_partials = 0, off_s = 0, off_x = 0, off_xt[2] = {0, 0}, off_sq[4] = {0, 0, 0, 0};
   int64_t stride_x = 0, stride_sq = 0;
   int mom_tiles_m = 0, mom_tiles_n = 0;
   double work = 0.0;
@@ -143,10 +145,11 @@ int choose_mode(int64_t m, int64_t n, const muon_hparams& hp) {
                                                                                       : MUON_NS_PLAIN;
 }
 
-// Tile configuration: 128 x 128 when the batch still gives every CU a couple of tiles,
-// else 64 x 64.
+// Tile configuration: 128 x 128 once a launch has at least half as many of them as the
+// GPU has CUs (measured on MI355X: the 128 tiles' deeper prefetch beats four times as many
+// 64 tiles from there on), else 64 x 64.
 int choose_tile(int64_t tiles128, int64_t count, int cu) {
-  return (tiles128 * count >= 2LL * cu) ? TILE_128 : TILE_64;
+  return (2 * tiles128 * count >= cu) ? TILE_128 : TILE_64;
 }
 
 int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams& hp,
@@ -199,8 +202,10 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
     g.off_s = off;
     off = align_up(off + sizeof(float) * cnt);
     g.stride_x = g.Mp * g.Np;
+    g.off_x = off;
+    off = align_up(off + ex * static_cast<size_t>(g.stride_x) * cnt);
     for (int k = 0; k < 2; ++k) {
-      g.off_x[k] = off;
+      g.off_xt[k] = off;
       off = align_up(off + ex * static_cast<size_t>(g.stride_x) * cnt);
     }
     g.stride_sq = g.Mp * g.Mp;
@@ -223,9 +228,9 @@ struct StepEnv {
   muon_ctx* ctx;
 };
 
-constexpr const char* kStageNames[] = {"table", "momentum", "norm_finalize", "syrk", "square",
-                                       "apply", "apply_update"};
-enum Stage { ST_TABLE, ST_MOMENTUM, ST_FINALIZE, ST_SYRK, ST_SQUARE, ST_APPLY, ST_UPDATE };
+constexpr const char* kStageNames[] = {"table", "momentum", "norm_finalize", "transpose", "syrk",
+                                       "square", "apply", "apply_update"};
+enum Stage { ST_TABLE, ST_MOMENTUM, ST_FINALIZE, ST_TRANSPOSE, ST_SYRK, ST_SQUARE, ST_APPLY, ST_UPDATE };
 constexpr size_t kMaxRecords = 1 << 16;
 
 // Brackets one launch with events when profiling is on (no effect otherwise).
@@ -282,7 +287,10 @@ void set_sym_tiles(GemmParams& p, int64_t Mp, int cfg) {
   p.tiles = nt * (nt + 1) / 2;
 }
 
-hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, float alpha, int spow) {
+// R = alpha * X X^T (symmetric). `input`: X is the momentum output (bf16 kernels on the
+// bf16 path), else the fp16 / fp32 iterate.
+hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, float alpha, int spow,
+                bool input) {
   GemmParams p = base_params(g, env);
   p.A = X; p.B = X; p.C = R;
   p.lda = p.ldb = g.Np; p.ldc = g.Mp;
@@ -292,7 +300,7 @@ hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, floa
   set_sym_tiles(p, g.Mp, g.tile_sq);
   const double cnt = static_cast<double>(p.count);
   StageTimer tm(env.ctx, env.st, ST_SYRK, g.m, g.n, p.count, cnt * g.m * g.m * g.n, 0.0);
-  const hipError_t e = launch_gemm(OP_SYRK, env.f32, g.tile_sq, p, env.st);
+  const hipError_t e = launch_gemm(input ? OP_SYRK_IN : OP_SYM, env.f32, g.tile_sq, p, env.st);
   tm.done();
   return e;
 }
@@ -309,22 +317,23 @@ hipError_t square(const Group& g, const StepEnv& env, const void* A, const void*
   set_sym_tiles(p, g.Mp, g.tile_sq);
   const double cnt = static_cast<double>(p.count);
   StageTimer tm(env.ctx, env.st, ST_SQUARE, g.m, g.n, p.count, cnt * g.m * g.m * g.m, 0.0);
-  const hipError_t e = launch_gemm(OP_SQUARE, env.f32, g.tile_sq, p, env.st);
+  const hipError_t e = launch_gemm(OP_SYM, env.f32, g.tile_sq, p, env.st);
   tm.done();
   return e;
 }
 
-// Xout = alpha * Q (bscale X) + beta X   (or the fused weight update when `update`).
-hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* X, void* Xout,
-                 float alpha, float bscale, int bspow, float beta, int beta_spow, bool use_e,
-                 bool update, const MatDesc* table) {
+// v = alpha * Q (XT)^T + beta * XT^T: writes X = oscale * v and XTout = oscale * v^T, or
+// (update) the weight update with O = v.
+hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* XT, void* X,
+                 void* XTout, float alpha, float beta, float oscale, bool use_e, bool update,
+                 const MatDesc* table) {
   GemmParams p = base_params(g, env);
-  p.A = Q; p.B = X; p.C = Xout; p.E = use_e ? X : nullptr;
-  p.lda = g.Mp; p.ldb = g.Np; p.ldc = g.Np; p.lde = g.Np;
-  p.sA = g.stride_sq; p.sB = g.stride_x; p.sC = g.stride_x; p.sE = g.stride_x;
+  p.A = Q; p.B = XT; p.C = X; p.C2 = XTout; p.E = use_e ? XT : nullptr;
+  p.e_trans = 1;
+  p.lda = g.Mp; p.ldb = g.Mp; p.ldc = g.Np; p.ldc2 = g.Mp; p.lde = g.Mp;
+  p.sA = g.stride_sq; p.sB = g.stride_x; p.sC = g.stride_x; p.sC2 = g.stride_x; p.sE = g.stride_x;
   p.M = static_cast<int32_t>(g.Mp); p.N = static_cast<int32_t>(g.Np); p.K = static_cast<int32_t>(g.Mp);
-  p.alpha = alpha; p.bscale = bscale; p.bscale_spow = bspow;
-  p.beta = beta; p.beta_spow = beta_spow;
+  p.alpha = alpha; p.beta = beta; p.oscale = oscale;
   const int t = g.tile_ap;
   p.tiles_m = static_cast<int32_t>((g.Mp + tile_bm(t) - 1) / tile_bm(t));
   p.tiles_n = static_cast<int32_t>((g.Np + tile_bn(t) - 1) / tile_bn(t));
@@ -352,45 +361,63 @@ hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* 
 int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
   const muon_hparams& hp = *env.hp;
   const bool f32 = env.f32;
-  // Momentum, canonical U (into X buffer 0) and per-tile partial sums of squares.
+  void* X = env.ws + g.off_x;
+  void* XT[2] = {env.ws + g.off_xt[0], env.ws + g.off_xt[1]};
+  const int count = static_cast<int32_t>(g.members.size());
+  float* s = reinterpret_cast<float*>(env.ws + g.off_s);
+
+  // Momentum, canonical U (into X) and per-tile partial sums of squares.
   MomentumParams mp;
   std::memset(&mp, 0, sizeof(mp));
   mp.table = table;
-  mp.U = env.ws + g.off_x[0];
+  mp.U = X;
   mp.sU = g.stride_x; mp.ldu = g.Np;
   mp.m = static_cast<int32_t>(g.m); mp.n = static_cast<int32_t>(g.n);
   mp.Mp = static_cast<int32_t>(g.Mp); mp.Np = static_cast<int32_t>(g.Np);
   mp.tiles_m = g.mom_tiles_m; mp.tiles_n = g.mom_tiles_n;
-  mp.count = static_cast<int32_t>(g.members.size());
+  mp.count = count;
   mp.mu = hp.momentum; mp.nesterov = hp.nesterov;
   mp.g_bf16 = hp.g_dtype == MUON_BF16; mp.m_bf16 = hp.m_dtype == MUON_BF16; mp.u_bf16 = !f32;
   mp.partials = reinterpret_cast<float*>(env.ws + g.off_partials);
   {
-    // algorithmic bytes: G read, M read + write, U written (canonical, padded)
+    // algorithmic bytes: G read, M read + write, U written
     const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;
     const double ub = f32 ? 4.0 : 2.0;
-    const double elems = static_cast<double>(mp.count) * g.m * g.n;
-    StageTimer tm(env.ctx, env.st, ST_MOMENTUM, g.m, g.n, mp.count, 0.0,
-                  elems * (gb + 2.0 * mb + ub));
+    const double elems = static_cast<double>(count) * g.m * g.n;
+    StageTimer tm(env.ctx, env.st, ST_MOMENTUM, g.m, g.n, count, 0.0, elems * (gb + 2.0 * mb + ub));
     MUON_HIP(launch_momentum(mp, env.st));
     tm.done();
   }
   {
-    StageTimer tm(env.ctx, env.st, ST_FINALIZE, g.m, g.n, mp.count, 0.0,
-                  4.0 * mp.count * g.mom_tiles_m * g.mom_tiles_n);
-    MUON_HIP(launch_norm_finalize(mp.partials, g.mom_tiles_m * g.mom_tiles_n, mp.count, hp.eps,
-                                  reinterpret_cast<float*>(env.ws + g.off_s), env.st));
+    StageTimer tm(env.ctx, env.st, ST_FINALIZE, g.m, g.n, count, 0.0,
+                  4.0 * count * g.mom_tiles_m * g.mom_tiles_n);
+    MUON_HIP(launch_norm_finalize(mp.partials, g.mom_tiles_m * g.mom_tiles_n, count, hp.eps, s, env.st));
     tm.done();
   }
 
-  // Scales of the bf16 path: Gram-like matrices (R, Q R, A) are kept multiplied by
-  // e ~ m' so their entries sit in fp16's normal range; the long operand X enters the
-  // fp16 apply multiplied by xs ~ sqrt(m' n') (both powers of two, so exact).
+  // Scales of the bf16 path (powers of two, so exact): the iterate X and its transposed
+  // copies are stored in fp16 multiplied by xs ~ sqrt(m' n') (entries ~ 1); the Gram-like
+  // matrices (R, Q R, A) are stored multiplied by e ~ m' so their entries sit in fp16's
+  // normal range; the polynomial coefficients absorb e.
   const float e = f32 ? 1.0f : pow2_near(static_cast<double>(g.m), 0, 14);
   const float xs = f32 ? 1.0f : pow2_near(std::sqrt(static_cast<double>(g.m) * g.n), 0, 14);
   const float a = hp.a, b1 = hp.b / e, c1 = hp.c / (e * e);
+  const float ixs = 1.0f / xs;
 
-  void* X[2] = {env.ws + g.off_x[0], env.ws + g.off_x[1]};
+  // X0^T = xs * s * U^T: the B operand of the first apply product.
+  {
+    TransposeParams tp;
+    std::memset(&tp, 0, sizeof(tp));
+    tp.U = X; tp.XT = XT[0];
+    tp.sU = g.stride_x; tp.sXT = g.stride_x;
+    tp.Mp = static_cast<int32_t>(g.Mp); tp.Np = static_cast<int32_t>(g.Np);
+    tp.count = count; tp.u_bf16 = !f32; tp.scale = xs; tp.s = s;
+    const double elems = static_cast<double>(count) * g.m * g.n;
+    StageTimer tm(env.ctx, env.st, ST_TRANSPOSE, g.m, g.n, count, 0.0, elems * (f32 ? 8.0 : 4.0));
+    MUON_HIP(launch_transpose_scale(tp, env.st));
+    tm.done();
+  }
+
   int cur = 0;
   if (g.mode == MUON_NS_PLAIN) {
     void* A = env.ws + g.off_sq[0];
@@ -398,10 +425,11 @@ int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
     const int rounds = total_rounds(hp);
     for (int r = 0; r < rounds; ++r) {
       const bool first = r == 0, last = r == rounds - 1;
-      MUON_HIP(syrk(g, env, X[cur], A, e, first ? 2 : 0));
-      MUON_HIP(square(g, env, A, A, A, B, c1, b1, 0.0f));
-      MUON_HIP(apply(g, env, B, X[cur], X[cur ^ 1], 1.0f / xs, xs, first ? 1 : 0, a, first ? 1 : 0,
-                     true, last, table));
+      // A' = e X X^T (first round: the momentum output, times s^2)
+      MUON_HIP(first ? syrk(g, env, X, A, e, 2, true) : syrk(g, env, X, A, e * ixs * ixs, 0, false));
+      MUON_HIP(square(g, env, A, A, A, B, c1, b1, 0.0f));           // B = b A + c A^2
+      // X' = a X + B X  (X taken from its transposed copy, which carries xs)
+      MUON_HIP(apply(g, env, B, XT[cur], X, XT[cur ^ 1], ixs, a * ixs, xs, true, last, table));
       cur ^= 1;
     }
   } else {
@@ -411,7 +439,7 @@ int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
     void* T2 = env.ws + g.off_sq[3];
     for (int sgi = 0; sgi < hp.n_segments; ++sgi) {
       const bool first = sgi == 0, last = sgi == hp.n_segments - 1;
-      MUON_HIP(syrk(g, env, X[cur], R, e, first ? 2 : 0));
+      MUON_HIP(first ? syrk(g, env, X, R, e, 2, true) : syrk(g, env, X, R, e * ixs * ixs, 0, false));
       MUON_HIP(square(g, env, R, R, R, Q, c1, b1, a));            // Q = P(R)
       for (int k = 1; k < hp.segments[sgi]; ++k) {
         MUON_HIP(square(g, env, Q, R, nullptr, T1, 1.0f, 0.0f, 0.0f));   // T = Q R
@@ -420,8 +448,7 @@ int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
         MUON_HIP(square(g, env, T1, Q, nullptr, T2, 1.0f, 0.0f, 0.0f));  // Q <- P Q
         std::swap(Q, T2);
       }
-      MUON_HIP(apply(g, env, Q, X[cur], X[cur ^ 1], 1.0f / xs, xs, first ? 1 : 0, 0.0f, 0, false,
-                     last, table));
+      MUON_HIP(apply(g, env, Q, XT[cur], X, XT[cur ^ 1], ixs, 0.0f, xs, false, last, table));
       cur ^= 1;
     }
   }
@@ -591,8 +618,8 @@ int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon
 }
 
 int muon_debug_gemm(muon_ctx* ctx, int kind, int ns_dtype, int tile, int64_t M, int64_t N, int64_t K,
-                    const void* A, const void* B, const void* E, void* C, float alpha, float beta,
-                    float gamma, float bscale, void* stream) {
+                    const void* A, const void* B, const void* E, void* C, void* C2, float alpha,
+                    float beta, float gamma, float oscale, void* stream) {
   try {
     if (kind == 0 && !B) B = A;  // X X^T: the second operand is X itself
     if (!ctx || !A || !B || !C) return MUON_ERR_ARG;
@@ -611,18 +638,19 @@ int muon_debug_gemm(muon_ctx* ctx, int kind, int ns_dtype, int tile, int64_t M, 
     p.A = A; p.B = B; p.C = C; p.E = E;
     p.M = static_cast<int32_t>(M); p.N = static_cast<int32_t>(N); p.K = static_cast<int32_t>(K);
     p.Mvalid = p.M; p.Nvalid = p.N;
-    p.alpha = alpha; p.beta = beta; p.gamma = gamma; p.bscale = bscale;
+    p.alpha = alpha; p.beta = beta; p.gamma = gamma; p.oscale = oscale;
+    p.lda = K; p.ldb = K;
     GemmOp op;
     if (kind == 2) {
       op = OP_APPLY;
-      p.lda = K; p.ldb = N; p.ldc = N; p.lde = N;
+      p.C2 = C2;
+      p.ldc = N; p.ldc2 = M; p.lde = M; p.e_trans = 1;
       p.tiles_m = static_cast<int32_t>((M + tile_bm(tile) - 1) / tile_bm(tile));
       p.tiles_n = static_cast<int32_t>((N + tile_bn(tile) - 1) / tile_bn(tile));
       p.tiles = p.tiles_m * p.tiles_n;
     } else {
-      op = kind == 0 ? OP_SYRK : OP_SQUARE;
-      if (kind == 0) B = A, p.B = A;
-      p.lda = K; p.ldb = K; p.ldc = N; p.lde = N;
+      op = kind == 0 ? OP_SYRK_IN : OP_SYM;
+      p.ldc = N; p.lde = N;
       const int nt = static_cast<int>((M + tile_bm(tile) - 1) / tile_bm(tile));
       p.tiles_m = p.tiles_n = nt;
       p.tiles = nt * (nt + 1) / 2;

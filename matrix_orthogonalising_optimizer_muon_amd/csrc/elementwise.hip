@@ -183,6 +183,52 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const float* partial
   if (threadIdx.x == 0) s[mat] = static_cast<float>(1.0 / (sqrt(red[0]) + static_cast<double>(eps)));
 }
 
+// 64 x 64 tile transpose through LDS: coalesced reads of U rows, coalesced writes of
+// X^T rows; the value is scaled by scale * s[mat] and converted (bf16 -> fp16 path).
+__global__ __launch_bounds__(kThreads) void transpose_scale_kernel(const TransposeParams p) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int mat = blockIdx.y;
+  const int tiles_n = p.Np / kTile;
+  const int ti = blockIdx.x / tiles_n, tj = blockIdx.x % tiles_n;
+  const int i0 = ti * kTile, j0 = tj * kTile;
+  const int tid = threadIdx.x;
+  const int cr = tid >> 3, cc = (tid & 7) * 8;
+  const float sc = p.scale * p.s[mat];
+  const int64_t ubase = static_cast<int64_t>(mat) * p.sU;
+#pragma unroll
+  for (int pass = 0; pass < kTile / 32; ++pass) {
+    const int lr = cr + pass * 32;
+    float v[8];
+    load8(p.U, ubase + static_cast<int64_t>(i0 + lr) * p.Np + j0 + cc, p.u_bf16, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[lr][cc + e] = v[e] * sc;
+  }
+  __syncthreads();
+  const int64_t xbase = static_cast<int64_t>(mat) * p.sXT;
+#pragma unroll
+  for (int pass = 0; pass < kTile / 32; ++pass) {
+    const int lr = cr + pass * 32;   // row of X^T = column of U
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[cc + e][lr];
+    const int64_t off = xbase + static_cast<int64_t>(j0 + lr) * p.Mp + i0 + cc;
+    if (p.u_bf16) {
+      unsigned int w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const _Float16 lo = static_cast<_Float16>(v[2 * q]), hi = static_cast<_Float16>(v[2 * q + 1]);
+        w[q] = static_cast<unsigned int>(__builtin_bit_cast(unsigned short, lo)) |
+               (static_cast<unsigned int>(__builtin_bit_cast(unsigned short, hi)) << 16);
+      }
+      *reinterpret_cast<uint4*>(static_cast<unsigned short*>(p.XT) + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.XT) + off);
+      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
 __global__ void write_table_kernel(const TableChunk c, MatDesc* dst) {
   const int i = threadIdx.x;
   if (i < c.n) dst[i] = c.d[i];
@@ -201,6 +247,13 @@ hipError_t launch_norm_finalize(const float* partials, int per_matrix, int count
                                 float* s, hipStream_t st) {
   if (count <= 0) return hipSuccess;
   hipLaunchKernelGGL(norm_finalize_kernel, dim3(count), dim3(256), 0, st, partials, per_matrix, eps, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_scale(const TransposeParams& p, hipStream_t st) {
+  if (p.count <= 0) return hipSuccess;
+  dim3 grid((p.Mp / kTile) * (p.Np / kTile), p.count);
+  hipLaunchKernelGGL(transpose_scale_kernel, grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -1,21 +1,24 @@
 // Batched MFMA GEMM family for the Newton-Schulz products on gfx950 (CDNA4).
 //
-// One kernel template serves every contraction of the update:
-//   * X X^T (the symmetric Gram product of the DMuon summary, section 2.2): NT operands,
-//     only upper tiles computed, off-diagonal tiles stored twice (mirrored);
-//   * the m' x m' products of the Gram recurrence and of A^2 (MuonX article, section
-//     3.2): NT operands (every operand is exactly symmetric in storage), symmetric output;
-//   * Q X / B X (the long "apply" product): NN, the row-major X tile is transposed in
-//     registers on its way to LDS, so every LDS tile is K-contiguous;
-//   * the last apply with the weight update fused into the epilogue.
+// Every contraction of the update is an NT product C = A B^T with both operands stored
+// K-contiguous (row-major, K = row length):
+//   * X X^T, the Gram matrix (DMuon summary, section 2.2: the symmetric Gram product):
+//     only upper tiles are computed, off-diagonal tiles are stored twice (mirrored);
+//   * the m' x m' products of the Gram recurrence and A^2 (MuonX article, section 3.2):
+//     every operand is exactly symmetric in storage, so A B = A B^T, and every result is
+//     symmetric in exact arithmetic: symmetric output as above;
+//   * the long "apply" product Q X, computed as Q (X^T)^T from the transposed copy X^T
+//     the previous stage keeps; its epilogue writes X' in both layouts (and adds a*X for
+//     plain NS), or, for the last product, updates W in place.
 //
-// Layout: a 256-thread workgroup (4 waves of 64) owns a BM x BN output tile; each wave a
-// (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks with fp32 accumulators. K advances in
-// 128-byte slices (64 bf16/fp16 or 32 fp32 elements), double-buffered in LDS, staged
-// through registers so the next slice's global loads overlap the current MFMAs. LDS rows
-// are 8 chunks of 16 bytes, XOR-swizzled per row so that both the fragment reads (32
-// consecutive rows, same chunk) and the transposed NN writes (rows 8 apart) spread over
-// all banks.
+// Layout: a workgroup of WM x WN waves (64 lanes each) owns a BM x BN output tile; each
+// wave a (BM/WM) x (BN/WN) sub-tile of 32x32x16 (bf16/fp16) or 32x32x2 (fp32) MFMA blocks
+// with fp32 accumulators. K advances in 128-byte slices, double-buffered in LDS and
+// staged through registers: the global loads of slice k + PF (PF = 1 or 2) are issued
+// before slice k's MFMAs, and slice k + 1 is written to the other LDS buffer half-way
+// through them. Fragments are double-buffered across the k-steps of a slice. LDS rows are 8 chunks of 16 bytes,
+// XOR-swizzled per row so that fragment reads of 32 consecutive rows spread over all
+// banks.
 #include <type_traits>
 
 #include "internal.hpp"
@@ -35,6 +38,13 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kChunks + (chunk ^ ((row ^ (row >> 3)) & 7));
 }
 
+__device__ __forceinline__ unsigned short f32_to_f16(float f) {
+  _Float16 h = static_cast<_Float16>(f);
+  return __builtin_bit_cast(unsigned short, h);
+}
+__device__ __forceinline__ float f16_to_f32(unsigned short h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
 __device__ __forceinline__ float bf16_to_f32(unsigned short h) {
   return __uint_as_float(static_cast<unsigned int>(h) << 16);
 }
@@ -43,13 +53,6 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   unsigned int u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<unsigned short>(u >> 16);
-}
-__device__ __forceinline__ unsigned short f32_to_f16(float f) {
-  _Float16 h = static_cast<_Float16>(f);
-  return __builtin_bit_cast(unsigned short, h);
-}
-__device__ __forceinline__ float f16_to_f32(unsigned short h) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
 __device__ __forceinline__ float scaled(float x, const float* s, int i, int pw) {
@@ -75,27 +78,97 @@ __device__ __forceinline__ void mma(f32x16& acc, const u32x4& a, const u32x4& b)
   }
 }
 
-// 16-bit 8x8 block transpose: in[r] holds 8 elements of row r; out[j] holds column j.
-__device__ __forceinline__ void transpose8x8_16(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    unsigned int lo[4], hi[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const unsigned int x = in[2 * p][q];
-      const unsigned int y = in[2 * p + 1][q];
-      lo[p] = __builtin_amdgcn_perm(y, x, 0x05040100u);  // (x.lo, y.lo): column 2q
-      hi[p] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // (x.hi, y.hi): column 2q+1
-    }
-    out[2 * q] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    out[2 * q + 1] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+// Output element type of a stage: fp32 on the fp32 path, fp16 on the bf16 path.
+template <int KIND>
+struct OutT {
+  using T = typename std::conditional<KIND == KIND_F32, float, unsigned short>::type;
+};
+
+template <typename T>
+__device__ __forceinline__ T to_out(float v) {
+  if constexpr (sizeof(T) == 4) return v;
+  else return f32_to_f16(v);
+}
+template <typename T>
+__device__ __forceinline__ float from_out(T v) {
+  if constexpr (sizeof(T) == 4) return v;
+  else return f16_to_f32(v);
+}
+
+// 4 consecutive elements at p (8 or 16 bytes; offsets are multiples of 4 elements).
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
+  if constexpr (sizeof(T) == 4) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    v[0] = f16_to_f32(x.x & 0xFFFFu); v[1] = f16_to_f32(x.x >> 16);
+    v[2] = f16_to_f32(x.y & 0xFFFFu); v[3] = f16_to_f32(x.y >> 16);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float (&v)[4], float scale) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
+  } else {
+    const u32x2 x{static_cast<unsigned int>(f32_to_f16(v[0] * scale)) |
+                      (static_cast<unsigned int>(f32_to_f16(v[1] * scale)) << 16),
+                  static_cast<unsigned int>(f32_to_f16(v[2] * scale)) |
+                      (static_cast<unsigned int>(f32_to_f16(v[3] * scale)) << 16)};
+    *reinterpret_cast<u32x2*>(p) = x;
   }
 }
 
-// 32-bit 4x4 block transpose.
-__device__ __forceinline__ void transpose4x4_32(const u32x4 (&in)[4], u32x4 (&out)[4]) {
+// W <- W*decay - lr*O for one lane's 16 values of a 32x32 block: rows rb + 8q + e
+// (q, e = 0..3) of column c in canonical orientation. All loads are issued before any
+// store; a transposed W holds the 4 rows of each q contiguously (16-byte accesses when
+// aligned).
+__device__ __forceinline__ void update_block(const GemmParams& p, const MatDesc& d, float decay, int c,
+                                             int rb, const float (&o)[4][4]) {
+  if (c >= p.Nvalid) return;
+  float w[4][4];
+  int64_t idx[4][4];
+  bool ok[4][4];
+  const bool vec = d.transposed && !p.w_bf16 && (d.cols % 4) == 0 &&
+                   (reinterpret_cast<uintptr_t>(d.W) % 16) == 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) out[j] = u32x4{in[0][j], in[1][j], in[2][j], in[3][j]};
+  for (int q = 0; q < 4; ++q) {
+    const int r0 = rb + q * 8;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + e;
+      ok[q][e] = r < p.Mvalid;
+      idx[q][e] = d.transposed ? static_cast<int64_t>(c) * d.cols + r : static_cast<int64_t>(r) * d.cols + c;
+    }
+    if (vec && r0 + 3 < p.Mvalid) {
+      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(d.W) + idx[q][0]);
+      w[q][0] = x.x; w[q][1] = x.y; w[q][2] = x.z; w[q][3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!ok[q][e]) { w[q][e] = 0.0f; continue; }
+        w[q][e] = p.w_bf16 ? bf16_to_f32(static_cast<const unsigned short*>(d.W)[idx[q][e]])
+                           : static_cast<const float*>(d.W)[idx[q][e]];
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float n[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) n[e] = w[q][e] * decay - p.lr * o[q][e];
+    if (vec && rb + q * 8 + 3 < p.Mvalid) {
+      *reinterpret_cast<float4*>(static_cast<float*>(d.W) + idx[q][0]) = make_float4(n[0], n[1], n[2], n[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!ok[q][e]) continue;
+        if (p.w_bf16) static_cast<unsigned short*>(d.W)[idx[q][e]] = f32_to_bf16(n[e]);
+        else static_cast<float*>(d.W)[idx[q][e]] = n[e];
+      }
+    }
+  }
 }
 
 // Tile index of this workgroup: XCD-aware remap, then grouped (8-tile-row) ordering for
@@ -125,22 +198,19 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
   }
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, bool NN, bool SYM, int EPI, typename TC>
+template <int KIND, int BM, int BN, int WM, int WN, int PF, bool SYM, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmParams p) {
+  static_assert(PF == 1 || PF == 2, "prefetch distance");
+  using TO = typename OutT<KIND>::T;
   constexpr int NT = 64 * WM * WN;                     // threads
-  constexpr int ES = (KIND == KIND_F32) ? 4 : 2;      // element bytes in LDS / MFMA
+  constexpr int ES = (KIND == KIND_F32) ? 4 : 2;      // operand element bytes
   constexpr int VEC = 16 / ES;                         // elements per 16-byte chunk
   constexpr int BK = kChunks * VEC;                    // k per LDS slice (128 bytes)
   constexpr int TWM = BM / WM, TWN = BN / WN;          // wave tile
   constexpr int FM = TWM / 32, FN = TWN / 32;          // 32x32 MFMA blocks per wave
   static_assert(FM >= 1 && FN >= 1, "wave tile");
-  constexpr int A_CH = (BM * kChunks + NT - 1) / NT;   // A chunks per thread
-  constexpr int B_CH = (BN * kChunks + NT - 1) / NT;   // NT B chunks per thread
-  // NN: the BK x BN slice of row-major B is cut into half-blocks of VEC/2 k-rows by VEC
-  // n-columns; each is transposed in registers into VEC 8-byte k-runs.
-  constexpr int HR = VEC / 2;
-  constexpr int N_HB = (BK / HR) * (BN / VEC);
-  constexpr int HB_T = (N_HB + NT - 1) / NT;
+  constexpr int A_CH = (BM * kChunks + NT - 1) / NT;   // staged A chunks per thread
+  constexpr int B_CH = (BN * kChunks + NT - 1) / NT;   // staged B chunks per thread
   constexpr int KSTEPS = kChunks / 2;                  // MFMA k-steps per slice
 
   __shared__ u32x4 lds[2][(BM + BN) * kChunks];
@@ -155,115 +225,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmParams p) 
   const int m0 = tm * BM, n0 = tn * BN;
 
   const char* Ab = static_cast<const char*>(p.A) + static_cast<int64_t>(mat) * p.sA * ES;
-  // NN B on the bf16 path is bf16 in memory (2 bytes) and converted to fp16.
   const char* Bb = static_cast<const char*>(p.B) + static_cast<int64_t>(mat) * p.sB * ES;
 
-  const float bscale = scaled(p.bscale, p.s, mat, p.bscale_spow);
-
-  // Global offsets (bytes, without k) of the chunks this thread stages. Rows past M or N
-  // are clamped to the last valid row: they only feed output rows/columns that are never
-  // stored, so the loads need no branches.
-  int64_t a_off[A_CH];
+  // Byte offsets (without k) of the chunks this thread stages. Rows past M or N are
+  // clamped to the last valid row: they only feed output rows/columns that are never
+  // stored, so the loads need no branches. K is a multiple of BK.
+  int64_t a_off[A_CH], b_off[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
     const int c = min(tid + i * NT, BM * kChunks - 1);
     const int gr = min(m0 + c / kChunks, p.M - 1);
     a_off[i] = (static_cast<int64_t>(gr) * p.lda + (c % kChunks) * VEC) * ES;
   }
-  int64_t b_off[NN ? HB_T : B_CH];
-  if constexpr (!NN) {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = min(tid + i * NT, BN * kChunks - 1);
-      const int gr = min(n0 + c / kChunks, p.N - 1);
-      b_off[i] = (static_cast<int64_t>(gr) * p.ldb + (c % kChunks) * VEC) * ES;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < HB_T; ++i) {
-      const int hb = min(tid + i * NT, N_HB - 1);
-      const int nb = hb % (BN / VEC), hk = hb / (BN / VEC);
-      const int gn = min(n0 + nb * VEC, p.N - VEC);
-      b_off[i] = (static_cast<int64_t>(hk * HR) * p.ldb + gn) * ES;
-    }
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = min(tid + i * NT, BN * kChunks - 1);
+    const int gr = min(n0 + c / kChunks, p.N - 1);
+    b_off[i] = (static_cast<int64_t>(gr) * p.ldb + (c % kChunks) * VEC) * ES;
   }
 
-  u32x4 ra[A_CH];
-  u32x4 rb[NN ? HB_T * HR : B_CH];
-
-  auto load_global = [&](int k0) {
-    const int64_t ka = static_cast<int64_t>(k0) * ES;
+  // PF staging register sets: slice k lands in set k % PF.
+  u32x4 ra[PF][A_CH], rb[PF][B_CH];
+  auto load_global = [&](int set, int k0) {
+    const int64_t kb = static_cast<int64_t>(k0) * ES;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(Ab + a_off[i] + ka);
-    if constexpr (!NN) {
+    for (int i = 0; i < A_CH; ++i) ra[set][i] = *reinterpret_cast<const u32x4*>(Ab + a_off[i] + kb);
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i] + ka);
-    } else {
-      const int64_t kb = static_cast<int64_t>(k0) * p.ldb * ES;
-#pragma unroll
-      for (int i = 0; i < HB_T; ++i)
-#pragma unroll
-        for (int r = 0; r < HR; ++r)
-          rb[i * HR + r] = *reinterpret_cast<const u32x4*>(Bb + b_off[i] + kb + static_cast<int64_t>(r) * p.ldb * ES);
-    }
+    for (int i = 0; i < B_CH; ++i) rb[set][i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i] + kb);
   };
-
-  auto store_lds = [&](int stage) {
+  auto store_lds = [&](int set, int stage) {
     u32x4* la = lds[stage];
     u32x4* lb = lds[stage] + BM * kChunks;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT;
-      if ((BM * kChunks) % NT == 0 || c < BM * kChunks) la[swz(c / kChunks, c % kChunks)] = ra[i];
+      if ((BM * kChunks) % NT == 0 || c < BM * kChunks) la[swz(c / kChunks, c % kChunks)] = ra[set][i];
     }
-    if constexpr (!NN) {
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * NT;
-        if ((BN * kChunks) % NT == 0 || c < BN * kChunks) lb[swz(c / kChunks, c % kChunks)] = rb[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < HB_T; ++i) {
-        const int hb = tid + i * NT;
-        if (N_HB % NT != 0 && hb >= N_HB) continue;
-        const int nb = hb % (BN / VEC), hk = hb / (BN / VEC);
-        const int kb = hk >> 1, half = hk & 1;
-        if constexpr (KIND == KIND_F16) {
-          // 4 bf16 rows of 8 -> scaled fp16, then 8 columns of 4 k-values.
-          unsigned int w[4][4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const unsigned int x = rb[i * HR + r][q];
-              const float lo = __uint_as_float(x << 16) * bscale;
-              const float hi = __uint_as_float(x & 0xFFFF0000u) * bscale;
-              w[r][q] = static_cast<unsigned int>(f32_to_f16(lo)) |
-                        (static_cast<unsigned int>(f32_to_f16(hi)) << 16);
-            }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            // columns 2q (low halves) and 2q+1 (high halves) of the 4 rows
-            const u32x2 lo{__builtin_amdgcn_perm(w[1][q], w[0][q], 0x05040100u),
-                           __builtin_amdgcn_perm(w[3][q], w[2][q], 0x05040100u)};
-            const u32x2 hi{__builtin_amdgcn_perm(w[1][q], w[0][q], 0x07060302u),
-                           __builtin_amdgcn_perm(w[3][q], w[2][q], 0x07060302u)};
-            reinterpret_cast<u32x2*>(&lb[swz(nb * 8 + 2 * q, kb)])[half] = lo;
-            reinterpret_cast<u32x2*>(&lb[swz(nb * 8 + 2 * q + 1, kb)])[half] = hi;
-          }
-        } else {
-          static_assert(KIND == KIND_F32, "NN operand kinds");
-          // 2 fp32 rows of 4 -> 4 columns of 2 k-values.
-          const u32x4 x0 = rb[i * HR], x1 = rb[i * HR + 1];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x2 v{__float_as_uint(__uint_as_float(x0[j]) * bscale),
-                          __float_as_uint(__uint_as_float(x1[j]) * bscale)};
-            reinterpret_cast<u32x2*>(&lb[swz(nb * 4 + j, kb)])[half] = v;
-          }
-        }
-      }
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * NT;
+      if ((BN * kChunks) % NT == 0 || c < BN * kChunks) lb[swz(c / kChunks, c % kChunks)] = rb[set][i];
     }
   };
 
@@ -288,14 +289,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmParams p) 
     for (int j = 0; j < FN; ++j) fb[buf][j] = lb[swz(wn0 + j * 32 + (lane & 31), ch)];
   };
 
-  // One 128-byte slice of K: fragments double-buffered across the k-steps; the staged
-  // next slice goes to the other LDS buffer half-way through.
-  auto slice = [&](int kt, auto has_next_tag) {
-    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+  // One 128-byte slice of K, read from LDS buffer kt % 2, fragments double-buffered
+  // across its k-steps. LOAD: issue the global loads of slice kt + PF into staging set
+  // kt % PF. STORE: half-way through, write slice kt + 1 (staging set (kt + 1) % PF) to
+  // the other LDS buffer. PH = kt % PF (a compile-time index into the staging sets).
+  auto slice = [&](int kt, auto load_tag, auto store_tag, auto ph_tag) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    constexpr bool STORE = decltype(store_tag)::value;
+    constexpr int PH = decltype(ph_tag)::value;
     const int stage = kt & 1;
     const u32x4* la = lds[stage];
     const u32x4* lb = lds[stage] + BM * kChunks;
-    if constexpr (HAS_NEXT) load_global((kt + 1) * BK);
+    if constexpr (LOAD) load_global(PH, (kt + PF) * BK);
     load_frags(0, la, lb, 0);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -304,30 +309,59 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmParams p) 
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) mma<KIND>(acc[i][j], fa[kk & 1][i], fb[kk & 1][j]);
-      if constexpr (HAS_NEXT) {
-        if (kk == KSTEPS / 2 - 1) store_lds(stage ^ 1);
+      if constexpr (STORE) {
+        if (kk == KSTEPS / 2 - 1) store_lds((PH + 1) % PF, stage ^ 1);
       }
     }
     __syncthreads();
   };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, (PF > 1) ? 1 : 0>;
 
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, std::true_type{});
-  slice(nk - 1, std::false_type{});
+  if constexpr (PF == 1) {
+    load_global(0, 0);
+    store_lds(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, T_{}, T_{}, P0{});
+    slice(nk - 1, F_{}, F_{}, P0{});
+  } else {
+    load_global(0, 0);
+    load_global(1, min(1, nk - 1) * BK);
+    store_lds(0, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 3 < nk; kt += 2) {
+      slice(kt, T_{}, T_{}, P0{});
+      slice(kt + 1, T_{}, T_{}, P1{});
+    }
+    const int left = nk - kt;  // 1, 2 or 3 slices, kt even
+    if (left == 3) {
+      slice(kt, T_{}, T_{}, P0{});
+      slice(kt + 1, F_{}, T_{}, P1{});
+      slice(kt + 2, F_{}, F_{}, P0{});
+    } else if (left == 2) {
+      slice(kt, F_{}, T_{}, P0{});
+      slice(kt + 1, F_{}, F_{}, P1{});
+    } else {
+      slice(kt, F_{}, F_{}, P0{});
+    }
+  }
 
-  // ---- epilogue ----
+  // ---- epilogue: per 32x32 block a lane holds column c, rows r0..r0+3 for q = 0..3 ----
   const float alpha = scaled(p.alpha, p.s, mat, p.alpha_spow);
   const float beta = scaled(p.beta, p.s, mat, p.beta_spow);
   const float gamma = p.gamma;
   const bool has_e = p.E != nullptr;
   const bool mirror = SYM && (tm != tn);
 
-  TC* C = nullptr;
-  const TC* E = nullptr;
-  if (EPI == EPI_STORE) C = static_cast<TC*>(p.C) + static_cast<int64_t>(mat) * p.sC;
-  if (has_e) E = static_cast<const TC*>(p.E) + static_cast<int64_t>(mat) * p.sE;
+  TO* C = nullptr;
+  TO* C2 = nullptr;
+  const TO* E = nullptr;
+  if (EPI != EPI_UPDATE) C = static_cast<TO*>(p.C) + static_cast<int64_t>(mat) * p.sC;
+  if (EPI == EPI_APPLY && p.C2 != nullptr) C2 = static_cast<TO*>(p.C2) + static_cast<int64_t>(mat) * p.sC2;
+  if (has_e) E = static_cast<const TO*>(p.E) + static_cast<int64_t>(mat) * p.sE;
 
   MatDesc d{};
   float decay = 1.0f;
@@ -341,70 +375,63 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmParams p) 
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int c = n0 + wn0 + j * 32 + (lane & 31);
+      float upd[4][4] = {};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        const int r0 = m0 + wm0 + i * 32 + q * 8 + (lane >> 5) * 4;
+        // M and N are multiples of 4: rows r0..r0+3 are all in range or all out.
+        if (r0 >= p.M || c >= p.N) continue;
+        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = m0 + wm0 + i * 32 + q * 8 + (lane >> 5) * 4 + e;
-          if (r >= p.M || c >= p.N) continue;
-          float v = alpha * acc[i][j][q * 4 + e];
-          if (has_e) {
-            const int64_t ei = static_cast<int64_t>(r) * p.lde + c;
-            if constexpr (sizeof(TC) == 4) {
-              v += beta * reinterpret_cast<const float*>(E)[ei];
-            } else {
-              const unsigned short h = reinterpret_cast<const unsigned short*>(E)[ei];
-              v += beta * ((EPI == EPI_UPDATE || !SYM) ? bf16_to_f32(h) : f16_to_f32(h));
-            }
-          }
-          if (r == c) v += gamma;
-          if constexpr (EPI == EPI_STORE) {
-            const int64_t ci = static_cast<int64_t>(r) * p.ldc + c;
-            const int64_t cm = static_cast<int64_t>(c) * p.ldc + r;
-            if constexpr (sizeof(TC) == 4) {
-              reinterpret_cast<float*>(C)[ci] = v;
-              if (mirror) reinterpret_cast<float*>(C)[cm] = v;
-            } else {
-              const unsigned short h = SYM ? f32_to_f16(v) : f32_to_bf16(v);
-              reinterpret_cast<unsigned short*>(C)[ci] = h;
-              if (mirror) reinterpret_cast<unsigned short*>(C)[cm] = h;
-            }
+        for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][q * 4 + e];
+        if (has_e) {
+          float ev[4];
+          if (p.e_trans) {
+            load4(E + static_cast<int64_t>(c) * p.lde + r0, ev);
           } else {
-            if (r < p.Mvalid && c < p.Nvalid) {
-              const int64_t wi = d.transposed ? static_cast<int64_t>(c) * d.cols + r
-                                              : static_cast<int64_t>(r) * d.cols + c;
-              if (p.w_bf16) {
-                unsigned short* W = static_cast<unsigned short*>(d.W);
-                W[wi] = f32_to_bf16(bf16_to_f32(W[wi]) * decay - p.lr * v);
-              } else {
-                float* W = static_cast<float*>(d.W);
-                W[wi] = W[wi] * decay - p.lr * v;
-              }
-            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ev[e] = from_out(E[static_cast<int64_t>(r0 + e) * p.lde + c]);
           }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += beta * ev[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (r0 + e == c) v[e] += gamma;
+        if constexpr (EPI == EPI_STORE || EPI == EPI_APPLY) {
+          const float os = (EPI == EPI_APPLY) ? p.oscale : 1.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) C[static_cast<int64_t>(r0 + e) * p.ldc + c] = to_out<TO>(v[e] * os);
+          if (SYM && mirror) store4(C + static_cast<int64_t>(c) * p.ldc + r0, v, 1.0f);
+          if (EPI == EPI_APPLY && C2 != nullptr) store4(C2 + static_cast<int64_t>(c) * p.ldc2 + r0, v, os);
+        } else {
+          upd[q][0] = v[0]; upd[q][1] = v[1]; upd[q][2] = v[2]; upd[q][3] = v[3];
         }
       }
+      if constexpr (EPI == EPI_UPDATE) update_block(p, d, decay, c, m0 + wm0 + i * 32 + (lane >> 5) * 4, upd);
     }
   }
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, bool NN, bool SYM, int EPI, typename TC>
+template <int KIND, int BM, int BN, int WM, int WN, int PF, bool SYM, int EPI>
 hipError_t launch_shape(const GemmParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, NN, SYM, EPI, TC>), dim3(p.tiles, p.count),
+  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, PF, SYM, EPI>), dim3(p.tiles, p.count),
                      dim3(64 * WM * WN), 0, st, p);
   return hipGetLastError();
 }
 
-template <int KIND, bool NN, bool SYM, int EPI, typename TC>
+template <int KIND, bool SYM, int EPI>
 hipError_t launch_tile(int cfg, const GemmParams& p, hipStream_t st) {
   switch (cfg) {
-    case TILE_64: return launch_shape<KIND, 64, 64, 2, 2, NN, SYM, EPI, TC>(p, st);
-    case TILE_128: return launch_shape<KIND, 128, 128, 2, 2, NN, SYM, EPI, TC>(p, st);
+    // 64 and 128 tiles keep two slices of loads in flight (few workgroups per CU must
+    // hide the load latency themselves); the 8-wave 256 tiles keep one.
+    case TILE_64: return launch_shape<KIND, 64, 64, 2, 2, 2, SYM, EPI>(p, st);
+    case TILE_128: return launch_shape<KIND, 128, 128, 2, 2, 2, SYM, EPI>(p, st);
     case TILE_256:  // 8 waves (2 per SIMD), wave tile 128 x 64
-      if constexpr (KIND != KIND_F32) return launch_shape<KIND, 256, 256, 2, 4, NN, SYM, EPI, TC>(p, st);
+      if constexpr (KIND != KIND_F32) return launch_shape<KIND, 256, 256, 2, 4, 1, SYM, EPI>(p, st);
       return hipErrorInvalidValue;
     case TILE_256x128:  // 8 waves, wave tile 64 x 64
-      if constexpr (!SYM && KIND != KIND_F32) return launch_shape<KIND, 256, 128, 4, 2, NN, SYM, EPI, TC>(p, st);
+      if constexpr (!SYM && KIND != KIND_F32) return launch_shape<KIND, 256, 128, 4, 2, 1, SYM, EPI>(p, st);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
@@ -416,17 +443,17 @@ hipError_t launch_gemm(GemmOp op, bool ns_f32, int cfg, const GemmParams& p, hip
   if (p.tiles <= 0 || p.count <= 0) return hipSuccess;
   if (ns_f32) {
     switch (op) {
-      case OP_SYRK:
-      case OP_SQUARE: return launch_tile<KIND_F32, false, true, EPI_STORE, float>(cfg, p, st);
-      case OP_APPLY: return launch_tile<KIND_F32, true, false, EPI_STORE, float>(cfg, p, st);
-      case OP_UPDATE: return launch_tile<KIND_F32, true, false, EPI_UPDATE, float>(cfg, p, st);
+      case OP_SYRK_IN:
+      case OP_SYM: return launch_tile<KIND_F32, true, EPI_STORE>(cfg, p, st);
+      case OP_APPLY: return launch_tile<KIND_F32, false, EPI_APPLY>(cfg, p, st);
+      case OP_UPDATE: return launch_tile<KIND_F32, false, EPI_UPDATE>(cfg, p, st);
     }
   } else {
     switch (op) {
-      case OP_SYRK: return launch_tile<KIND_BF16, false, true, EPI_STORE, unsigned short>(cfg, p, st);
-      case OP_SQUARE: return launch_tile<KIND_F16, false, true, EPI_STORE, unsigned short>(cfg, p, st);
-      case OP_APPLY: return launch_tile<KIND_F16, true, false, EPI_STORE, unsigned short>(cfg, p, st);
-      case OP_UPDATE: return launch_tile<KIND_F16, true, false, EPI_UPDATE, unsigned short>(cfg, p, st);
+      case OP_SYRK_IN: return launch_tile<KIND_BF16, true, EPI_STORE>(cfg, p, st);
+      case OP_SYM: return launch_tile<KIND_F16, true, EPI_STORE>(cfg, p, st);
+      case OP_APPLY: return launch_tile<KIND_F16, false, EPI_APPLY>(cfg, p, st);
+      case OP_UPDATE: return launch_tile<KIND_F16, false, EPI_UPDATE>(cfg, p, st);
     }
   }
   return hipErrorInvalidValue;

@@ -17,41 +17,43 @@ struct MatDesc {
 };
 
 enum Kind : int { KIND_BF16 = 0, KIND_F16 = 1, KIND_F32 = 2 };
-enum Epi : int { EPI_STORE = 0, EPI_UPDATE = 1 };
+enum Epi : int { EPI_STORE = 0, EPI_APPLY = 1, EPI_UPDATE = 2 };
 
-// Batched GEMM over `count` same-shape problems. Matrix i of the batch uses
-// A + i*sA, B + i*sB, C + i*sC, E + i*sE (element strides) and scalar s[i].
-//   NT (B is N x K row-major):  acc = A * B^T
-//   NN (B is K x N row-major):  acc = A * (bscale' * B)   (B converted to A's type)
-// Epilogue: out = alpha' * acc + beta' * E + gamma * [row == col]
-//   with alpha' = alpha * s[i]^alpha_spow, beta' = beta * s[i]^beta_spow,
-//   bscale' = bscale * s[i]^bscale_spow.
-// SYM: only tiles with tile_m <= tile_n are computed; off-diagonal tiles are also
-// stored mirrored, so C is exactly symmetric.
-// EPI_UPDATE: out is O in canonical orientation; W[desc] <- W*(1 - lr*wd) - lr*O for
-// row < Mvalid, col < Nvalid, through the descriptor's orientation.
+// Batched NT GEMM over `count` same-shape problems: acc = A * B^T with A (M x K) and
+// B (N x K) row-major. Matrix i of the batch uses A + i*sA, B + i*sB, ... (element
+// strides) and the device scalar s[i].
+// Epilogue value: v = alpha' * acc + beta' * E + gamma * [row == col], with
+//   alpha' = alpha * s[i]^alpha_spow, beta' = beta * s[i]^beta_spow, and E read at
+//   (row, col) or, with e_trans, at (col, row).
+//   EPI_STORE (symmetric output): C = v; only tiles with tile_m <= tile_n are computed
+//     and off-diagonal tiles are also stored mirrored, so C is exactly symmetric.
+//   EPI_APPLY: C = oscale * v and, if C2, C2^T = oscale * v (transposed copy).
+//   EPI_UPDATE: W[desc] <- W*(1 - lr*wd) - lr*v for row < Mvalid, col < Nvalid, through
+//     the descriptor's orientation.
+// M, N, K are multiples of 64 (the padded canonical sizes).
 struct GemmParams {
-  const void* A; const void* B; void* C; const void* E;
-  int64_t lda, ldb, ldc, lde;
-  int64_t sA, sB, sC, sE;
+  const void* A; const void* B; void* C; void* C2; const void* E;
+  int64_t lda, ldb, ldc, ldc2, lde;
+  int64_t sA, sB, sC, sC2, sE;
   int32_t M, N, K;
   int32_t Mvalid, Nvalid;
   int32_t tiles_m, tiles_n, tiles;
   int32_t count;
-  float alpha, beta, gamma, bscale;
-  int32_t alpha_spow, beta_spow, bscale_spow;
+  float alpha, beta, gamma, oscale;
+  int32_t alpha_spow, beta_spow;
+  int32_t e_trans;
   const float* s;
   const MatDesc* table;   // EPI_UPDATE: descriptors of the batch (entry i = matrix i)
   float lr, wd;
   int32_t w_bf16;
 };
 
-// Stage identifiers of the GEMM family.
+// Stages of the GEMM family.
 enum GemmOp : int {
-  OP_SYRK = 0,     // C = X X^T, symmetric (NT, A = B = X)
-  OP_SQUARE = 1,   // C = A B^T with symmetric output (NT)
-  OP_APPLY = 2,    // C = A B (NN), general output
-  OP_UPDATE = 3,   // as OP_APPLY, epilogue updates W
+  OP_SYRK_IN = 0,  // X X^T on the momentum output (bf16 on the bf16 path), symmetric
+  OP_SYM = 1,      // A B^T with symmetric output (fp16 / fp32 operands)
+  OP_APPLY = 2,    // A B^T, general output, X in both layouts
+  OP_UPDATE = 3,   // A B^T, epilogue updates W
 };
 
 // Workgroup tile configurations (4 waves each). Symmetric-output stages need BM == BN.
@@ -83,6 +85,20 @@ struct MomentumParams {
   float* partials;        // [count][tiles_m*tiles_n]
 };
 hipError_t launch_momentum(const MomentumParams& p, hipStream_t st);
+
+// XT[i] = scale * s[i] * U[i]^T: the transposed, scaled copy of the momentum output the
+// first apply product reads (fp16 on the bf16 path, fp32 on the fp32 path).
+struct TransposeParams {
+  const void* U;          // Mp x Np, ld Np, bf16 or fp32
+  void* XT;               // Np x Mp, ld Mp, fp16 or fp32
+  int64_t sU, sXT;        // element strides between matrices
+  int32_t Mp, Np;
+  int32_t count;
+  int32_t u_bf16;         // U bf16 (then XT fp16) or fp32 (then XT fp32)
+  float scale;
+  const float* s;
+};
+hipError_t launch_transpose_scale(const TransposeParams& p, hipStream_t st);
 
 // s[i] = 1 / (sqrt(sum_j partials[i][j]) + eps), fixed-order fp64 reduction.
 hipError_t launch_norm_finalize(const float* partials, int per_matrix, int count, float eps,

@@ -164,13 +164,14 @@ def test_workspace_errors(hctx):
 def test_debug_gemm_validation(hctx):
     f = B._lib.muon_debug_gemm
     P = ctypes.c_void_p(FAKE)
-    # f(ctx, kind, ns_dtype, tile_cfg, M, N, K, A, B, E, C, alpha, beta, gamma, bscale, stream)
-    assert f(hctx, 3, 1, 0, 64, 64, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
-    assert f(hctx, 0, 1, 4, 64, 64, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
-    assert f(hctx, 0, 1, 0, 64, 64, 100, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
-    assert f(hctx, 1, 1, 0, 64, 128, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
-    assert f(hctx, 0, 1, 2, 256, 256, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
-    assert f(hctx, 2, 1, 2, 64, 128, 64, P, P, None, P, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_DEVICE
+    # f(ctx, kind, ns_dtype, tile_cfg, M, N, K, A, B, E, C, C2, alpha, beta, gamma, oscale, stream)
+    assert f(hctx, 3, 1, 0, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 0, 1, 4, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 0, 1, 0, 64, 64, 100, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 1, 1, 0, 64, 128, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 0, 1, 2, 256, 256, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 2, 1, 0, 64, 64, 64, P, P, None, None, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 2, 1, 2, 64, 128, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_DEVICE
 
 
 # ---------------------------------------------------------------- dispatcher / FLOP model

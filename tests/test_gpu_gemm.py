@@ -1,5 +1,6 @@
 """Per-stage parity of the MFMA GEMM kernels (test-only entry point muon_debug_gemm)
-against float64 products of the exact operand values the kernel consumed.
+against float64 products of the exact operand values the kernel consumed. Every product
+is A B^T with both operands K-contiguous.
 
 Tolerances: the output is rounded once to its storage type (fp16: 2^-11, bf16: 2^-8
 relative) after fp32 accumulation, so each element is checked against
@@ -63,7 +64,7 @@ def test_syrk_bf16(B, ctx, tile, M, K):
     X = bf16_round(rng.standard_normal((M, K)))
     C = torch.empty((M, M), dtype=torch.float16, device="cuda")
     alpha = 0.25
-    assert B.muon_debug_gemm(ctx, 0, "bf16", tile, M, M, K, dev(X, torch.bfloat16), None, None, C, alpha) == 0
+    assert B.muon_debug_gemm(ctx, 0, "bf16", tile, M, M, K, dev(X, torch.bfloat16), None, None, C, alpha=alpha) == 0
     torch.cuda.synchronize()
     got = host(C)
     ref = alpha * (X @ X.T)
@@ -77,7 +78,7 @@ def test_syrk_f32(B, ctx, tile, M, K):
     rng = np.random.default_rng(M + K + tile)
     X = rng.standard_normal((M, K)).astype(np.float32).astype(np.float64)
     C = torch.empty((M, M), dtype=torch.float32, device="cuda")
-    assert B.muon_debug_gemm(ctx, 0, "f32", tile, M, M, K, dev(X, torch.float32), None, None, C, 1.0) == 0
+    assert B.muon_debug_gemm(ctx, 0, "f32", tile, M, M, K, dev(X, torch.float32), None, None, C) == 0
     torch.cuda.synchronize()
     got = host(C)
     ref = X @ X.T
@@ -98,7 +99,7 @@ def test_square_poly(B, ctx, tile, ns, dt, u):
     A = dev(S, dt)
     C = torch.empty((M, M), dtype=dt, device="cuda")
     alpha, beta, gamma = 0.5, -1.25, 3.0
-    assert B.muon_debug_gemm(ctx, 1, ns, tile, M, M, M, A, A, A, C, alpha, beta, gamma) == 0
+    assert B.muon_debug_gemm(ctx, 1, ns, tile, M, M, M, A, A, A, C, alpha=alpha, beta=beta, gamma=gamma) == 0
     torch.cuda.synchronize()
     got = host(C)
     ref = alpha * (S @ S.T) + beta * S + gamma * np.eye(M)
@@ -106,23 +107,40 @@ def test_square_poly(B, ctx, tile, ns, dt, u):
     assert np.array_equal(got, got.T)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3])
-@pytest.mark.parametrize("M,N,K", [(128, 320, 192), (256, 1024, 256), (64, 64, 64), (384, 704, 320)])
-def test_apply_bf16(B, ctx, tile, M, N, K):
-    rng = np.random.default_rng(M + N + K + tile)
-    Q = f16_round(rng.standard_normal((M, K)))
-    X = bf16_round(rng.standard_normal((K, N)) * 0.01)
-    E = bf16_round(rng.standard_normal((M, N)) * 0.01)
-    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    alpha, beta, bscale = 1.0 / 64, 0.75, 64.0
-    assert B.muon_debug_gemm(ctx, 2, "bf16", tile, M, N, K, dev(Q, torch.float16), dev(X, torch.bfloat16),
-                             dev(E, torch.bfloat16), C, alpha, beta, 0.0, bscale) == 0
+@pytest.mark.parametrize("tile", [0, 1, 3])
+@pytest.mark.parametrize("M,K", [(128, 576), (320, 192)])
+def test_sym_long_fp16(B, ctx, tile, M, K):
+    """kind 1 with A = B = X (M x K, K != M): the Gram product of the fp16 iterate."""
+    rng = np.random.default_rng(M + 7 * K + tile)
+    X = f16_round(rng.standard_normal((M, K)) * 4.0)
+    Xd = dev(X, torch.float16)
+    C = torch.empty((M, M), dtype=torch.float16, device="cuda")
+    assert B.muon_debug_gemm(ctx, 1, "bf16", tile, M, M, K, Xd, Xd, None, C, alpha=1.0 / 256) == 0
     torch.cuda.synchronize()
     got = host(C)
-    Xh = f16_round(X * bscale)  # the fp16 operand the kernel builds from bf16 X
-    ref = alpha * (Q @ Xh) + beta * E
-    check_elems(got, ref, K, 2.0 ** -8)
-    assert rel(got, ref) < 4e-3
+    check_elems(got, (X @ X.T) / 256, K, 2.0 ** -11)
+    assert np.array_equal(got, got.T)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+@pytest.mark.parametrize("M,N,K", [(128, 320, 192), (256, 1024, 256), (64, 64, 64), (384, 704, 320)])
+def test_apply_fp16(B, ctx, tile, M, N, K):
+    """kind 2: v = alpha A B^T + beta E^T; C = oscale v and C2 = oscale v^T (fp16)."""
+    rng = np.random.default_rng(M + N + K + tile)
+    Q = f16_round(rng.standard_normal((M, K)))
+    XT = f16_round(rng.standard_normal((N, K)) * 8.0)
+    ET = f16_round(rng.standard_normal((N, M)) * 8.0)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    C2 = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    alpha, beta, oscale = 1.0 / 64, 0.75 / 64, 64.0
+    assert B.muon_debug_gemm(ctx, 2, "bf16", tile, M, N, K, dev(Q, torch.float16), dev(XT, torch.float16),
+                             dev(ET, torch.float16), C, C2, alpha=alpha, beta=beta, oscale=oscale) == 0
+    torch.cuda.synchronize()
+    ref = oscale * (alpha * (Q @ XT.T) + beta * ET.T)
+    got, got2 = host(C), host(C2)
+    check_elems(got, ref, K, 2.0 ** -11)
+    assert np.array_equal(got2, got.T)   # both layouts hold the same rounded values
+    assert rel(got, ref) < 1e-3
 
 
 @pytest.mark.parametrize("tile", [0, 1])
@@ -130,17 +148,20 @@ def test_apply_f32(B, ctx, tile):
     M, N, K = 192, 448, 128
     rng = np.random.default_rng(tile + 5)
     Q = rng.standard_normal((M, K)).astype(np.float32).astype(np.float64)
-    X = rng.standard_normal((K, N)).astype(np.float32).astype(np.float64)
+    XT = rng.standard_normal((N, K)).astype(np.float32).astype(np.float64)
     C = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    assert B.muon_debug_gemm(ctx, 2, "f32", tile, M, N, K, dev(Q, torch.float32), dev(X, torch.float32),
-                             None, C, 2.0, 0.0, 0.0, 0.5) == 0
+    C2 = torch.empty((N, M), dtype=torch.float32, device="cuda")
+    assert B.muon_debug_gemm(ctx, 2, "f32", tile, M, N, K, dev(Q, torch.float32), dev(XT, torch.float32),
+                             None, C, C2, alpha=2.0, oscale=0.5) == 0
     torch.cuda.synchronize()
     got = host(C)
-    ref = 2.0 * (Q @ (X * 0.5))
+    ref = Q @ XT.T
     check_elems(got, ref, K, 2.0 ** -24)
+    assert np.array_equal(host(C2), got.T)
 
 
 def test_unavailable_tile_config(B, ctx):
     X = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
     assert B.muon_debug_gemm(ctx, 0, "f32", 3, 64, 64, 64, X, None, None, X) == B.MUON_ERR_UNSUPPORTED
+    assert B.muon_debug_gemm(ctx, 2, "f32", 2, 64, 64, 64, X, X, None, X) == B.MUON_ERR_UNSUPPORTED
     assert B.muon_debug_gemm(ctx, 0, "bf16", 2, 64, 64, 64, X, None, None, X) == B.MUON_ERR_ARG

@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--details", action="store_true", help="also print the per-stage table to stderr")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before warmup, copy this many MiB device-to-device once (a plain copy "
+                         "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -128,6 +131,17 @@ def main():
 
     def step(c):
         B.check(B.muon_step(c, arr, hp, ws.data_ptr(), nbytes, sp, count=len(mats)), "muon_step")
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.calibrate_copy_mib} MiB read + written", file=sys.stderr,
+              flush=True)
+        del src, dst
 
     for _ in range(args.warmup):
         step(ctx)

@@ -164,6 +164,9 @@ def main():
           file=sys.stderr, flush=True)
 
     # Second pass with per-launch events (library profiler) for the per-kernel roofline.
+    step(pctx)  # warm-up of the profiling context (tile choices are already cached)
+    torch.cuda.synchronize()
+    B.muon_profile_read(pctx, 4096)
     for _ in range(args.steps):
         step(pctx)
     torch.cuda.synchronize()
@@ -217,6 +220,15 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    plans = {}
+    for i, spec in enumerate(w.matrices):
+        key = f"{min(spec.rows, spec.cols)}x{max(spec.rows, spec.cols)}"
+        if key in plans:
+            continue
+        e = B.muon_plan_info(ctx, mats, hp, i)
+        plans[key] = {"mode": {1: "plain", 2: "gram"}[e.mode], "tile_sym": e.tile_sym,
+                      "tile_apply": e.tile_apply}
+    out["config"]["plan"] = plans
     B.muon_destroy(ctx)
     B.muon_destroy(pctx)
     print(json.dumps(out), flush=True)

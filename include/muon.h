@@ -52,7 +52,7 @@ extern "C" {
 #define MUON_MAX_SEGMENTS 8
 
 /* ---- muon_init flags ---- */
-#define MUON_FLAG_MODEL_ONLY 1u  /* dispatcher uses the FLOP model only (no timed tuning) */
+#define MUON_FLAG_MODEL_ONLY 1u  /* no timed tile tuning: static tile choice only */
 #define MUON_FLAG_PROFILE 2u     /* bracket every launch with hipEvents (muon_profile_read) */
 
 typedef struct muon_ctx muon_ctx; /* opaque; owned by the library */
@@ -103,7 +103,10 @@ typedef struct muon_plan_entry {
   int32_t transposed;    /* 1 if rows > cols (processed as the transpose) */
   int64_t m, n;          /* canonical short side m' and long side n' */
   int32_t group;         /* same-shape group index (one batched launch per stage) */
-  int32_t tile;          /* tile rows of the apply GEMM kernel used (64, 128 or 256) */
+  int32_t tile_sym;      /* tile configuration of the m' x m' products (muon_debug_gemm ids):
+                            the measured choice once a step has run, else the static one */
+  int32_t tile_apply;    /* tile configuration of the apply products, likewise */
+  int32_t reserved;
   double dense_flops;    /* matmul FLOPs as the MuonX article counts them (2m'^2n', 2m'^3) */
   double kernel_flops;   /* FLOPs the kernels actually perform (symmetric outputs halved) */
 } muon_plan_entry;
@@ -146,7 +149,12 @@ int muon_workspace_size(muon_ctx *ctx, const muon_matrix *mats, int count,
  * bytes, 256-byte aligned, owned by the caller and not used by anything else until the
  * step completes. Each matrix's result equals a separate call for it (grouping only
  * batches launches). Launch failures return MUON_ERR_HIP; device faults surface at the
- * caller's next synchronisation. A context must not be used by two threads at once. */
+ * caller's next synchronisation. A context must not be used by two threads at once.
+ * Shape-adaptive tiles (DMuon summary, section 2.4: per-shape kernel configurations,
+ * measured once and cached): unless the context has MUON_FLAG_MODEL_ONLY, the first
+ * step that meets a new (stage, shape, batch) times the candidate tile configurations on
+ * its own workspace buffers, synchronising the stream once for it, and caches the
+ * fastest for the process; later steps make no host synchronisation. */
 int muon_step(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hparams *hp,
               void *workspace, size_t workspace_bytes, void *stream);
 

@@ -64,7 +64,8 @@ class muon_hparams(ctypes.Structure):
 class muon_plan_entry(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("transposed", ctypes.c_int32),
                 ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("group", ctypes.c_int32),
-                ("tile", ctypes.c_int32), ("dense_flops", ctypes.c_double),
+                ("tile_sym", ctypes.c_int32), ("tile_apply", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("dense_flops", ctypes.c_double),
                 ("kernel_flops", ctypes.c_double)]
 
 

@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <tuple>
@@ -40,6 +41,7 @@ struct muon_ctx {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> event_pool;
   std::vector<ProfRecord> records;
   size_t next_event = 0;
+  hipEvent_t tune_ev[2] = {nullptr, nullptr};  // events of the tile measurements
 };
 
 namespace muon {
@@ -145,11 +147,18 @@ int choose_mode(int64_t m, int64_t n, const muon_hparams& hp) {
                                                                                       : MUON_NS_PLAIN;
 }
 
-// Tile configuration: 128 x 128 once a launch has at least half as many of them as the
-// GPU has CUs (measured on MI355X: the 128 tiles' deeper prefetch beats four times as many
-// 64 tiles from there on), else 64 x 64.
-int choose_tile(int64_t tiles128, int64_t count, int cu) {
-  return (2 * tiles128 * count >= cu) ? TILE_128 : TILE_64;
+// Static tile choice (MUON_FLAG_MODEL_ONLY, and the default before a measurement):
+// symmetric stages use 128 x 128 once a launch has at least half as many of them as the
+// GPU has CUs, else 64 x 64; the apply uses 256 x 256 once there is one per CU.
+int heuristic_sym(int64_t Mp, int64_t count, int cu) {
+  const int64_t nt = (Mp + 127) / 128;
+  return (2 * (nt * (nt + 1) / 2) * count >= cu) ? TILE_128 : TILE_64;
+}
+int heuristic_apply(int64_t Mp, int64_t Np, int64_t count, int cu, bool f32) {
+  const int64_t t256 = ((Mp + 255) / 256) * ((Np + 255) / 256);
+  if (!f32 && Mp >= 256 && t256 * count >= cu) return TILE_256_DMA;
+  const int64_t t128 = ((Mp + 127) / 128) * ((Np + 127) / 128);
+  return (2 * t128 * count >= cu) ? TILE_128 : TILE_64;
 }
 
 int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams& hp,
@@ -176,8 +185,9 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
       g.members.assign(all.begin() + b, all.begin() + std::min(all.size(), b + kMaxBatch));
       const int64_t cnt = static_cast<int64_t>(g.members.size());
       const int64_t nt_sq = (g.Mp + 127) / 128;
-      g.tile_sq = choose_tile(nt_sq * (nt_sq + 1) / 2, cnt, ctx->cu_count);
-      g.tile_ap = choose_tile(((g.Mp + 127) / 128) * ((g.Np + 127) / 128), cnt, ctx->cu_count);
+      g.tile_sq = heuristic_sym(g.Mp, cnt, ctx->cu_count);
+      g.tile_ap = heuristic_apply(g.Mp, g.Np, cnt, ctx->cu_count, f32);
+      (void)nt_sq;
       g.work = kernel_flops(m, n, g.mode, hp) * cnt;
       plan.groups.push_back(std::move(g));
     }
@@ -287,20 +297,86 @@ void set_sym_tiles(GemmParams& p, int64_t Mp, int cfg) {
   p.tiles = nt * (nt + 1) / 2;
 }
 
+// Launch a GEMM stage with the tile configuration measured for it. On the first launch
+// of a (stage, path, shape, batch) the candidates are timed on the stage's own buffers
+// (one warm-up and one timed launch each; the stream is synchronised for it) and the
+// fastest is cached in the context; MUON_FLAG_MODEL_ONLY keeps the static choice. A
+// stage that updates W is timed through its apply twin, which writes only workspace.
+// Measured tile configurations, shared by every context of the process:
+// (device, stage, path, padded m', padded n' or m', batch) -> TileCfg.
+using TuneKey = std::tuple<int, int, int, int64_t, int64_t, int>;
+std::mutex g_tune_mu;
+std::map<TuneKey, int> g_tuned;
+
+template <class Build>
+hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristic, bool sym,
+                     Build build) {
+  muon_ctx* ctx = env.ctx;
+  int cfg = heuristic;
+  if (!(ctx->flags & MUON_FLAG_MODEL_ONLY)) {
+    const int key_op = (op == OP_UPDATE) ? OP_APPLY : op;
+    const TuneKey key = std::make_tuple(ctx->device, key_op, env.f32 ? 1 : 0, g.Mp, sym ? g.Mp : g.Np,
+                                        static_cast<int>(g.members.size()));
+    bool found = false;
+    {
+      std::lock_guard<std::mutex> lk(g_tune_mu);
+      auto it = g_tuned.find(key);
+      if (it != g_tuned.end()) { cfg = it->second; found = true; }
+    }
+    if (!found) {
+      std::vector<int> cands;
+      if (env.f32) {
+        cands = {TILE_64, TILE_128, TILE_64_DMA, TILE_128_DMA};
+      } else if (sym) {
+        cands = {TILE_64, TILE_128, TILE_128_DMA};
+        if (g.Mp >= 512) cands.push_back(TILE_256_DMA);
+      } else {
+        cands = {TILE_64, TILE_128};
+        if (g.Mp >= 256) {
+          cands.push_back(TILE_256x128_DMA);
+          cands.push_back(TILE_256_DMA);
+        }
+      }
+      for (int i = 0; i < 2; ++i)
+        if (!ctx->tune_ev[i] && hipEventCreate(&ctx->tune_ev[i]) != hipSuccess) return hipErrorUnknown;
+      const GemmOp top = (op == OP_UPDATE) ? OP_APPLY : op;
+      float best = 1e30f;
+      for (int c : cands) {
+        const GemmParams p = build(c);
+        if (launch_gemm(top, env.f32, c, p, env.st) != hipSuccess) continue;  // warm-up
+        if (hipEventRecord(ctx->tune_ev[0], env.st) != hipSuccess) return hipErrorUnknown;
+        if (launch_gemm(top, env.f32, c, p, env.st) != hipSuccess) return hipErrorUnknown;
+        if (hipEventRecord(ctx->tune_ev[1], env.st) != hipSuccess) return hipErrorUnknown;
+        if (hipEventSynchronize(ctx->tune_ev[1]) != hipSuccess) return hipErrorUnknown;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, ctx->tune_ev[0], ctx->tune_ev[1]) != hipSuccess) return hipErrorUnknown;
+        if (ms < best) { best = ms; cfg = c; }
+      }
+      std::lock_guard<std::mutex> lk(g_tune_mu);
+      g_tuned[key] = cfg;
+    }
+  }
+  const GemmParams p = build(cfg);
+  return launch_gemm(op, env.f32, cfg, p, env.st);
+}
+
 // R = alpha * X X^T (symmetric). `input`: X is the momentum output (bf16 kernels on the
 // bf16 path), else the fp16 / fp32 iterate.
 hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, float alpha, int spow,
                 bool input) {
-  GemmParams p = base_params(g, env);
-  p.A = X; p.B = X; p.C = R;
-  p.lda = p.ldb = g.Np; p.ldc = g.Mp;
-  p.sA = p.sB = g.stride_x; p.sC = g.stride_sq;
-  p.M = p.N = static_cast<int32_t>(g.Mp); p.K = static_cast<int32_t>(g.Np);
-  p.alpha = alpha; p.alpha_spow = spow;
-  set_sym_tiles(p, g.Mp, g.tile_sq);
-  const double cnt = static_cast<double>(p.count);
-  StageTimer tm(env.ctx, env.st, ST_SYRK, g.m, g.n, p.count, cnt * g.m * g.m * g.n, 0.0);
-  const hipError_t e = launch_gemm(input ? OP_SYRK_IN : OP_SYM, env.f32, g.tile_sq, p, env.st);
+  auto build = [&](int cfg) {
+    GemmParams p = base_params(g, env);
+    p.A = X; p.B = X; p.C = R;
+    p.lda = p.ldb = g.Np; p.ldc = g.Mp;
+    p.sA = p.sB = g.stride_x; p.sC = g.stride_sq;
+    p.M = p.N = static_cast<int32_t>(g.Mp); p.K = static_cast<int32_t>(g.Np);
+    p.alpha = alpha; p.alpha_spow = spow;
+    set_sym_tiles(p, g.Mp, cfg);
+    return p;
+  };
+  const double cnt = static_cast<double>(g.members.size());
+  StageTimer tm(env.ctx, env.st, ST_SYRK, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.n, 0.0);
+  const hipError_t e = run_stage(env, g, input ? OP_SYRK_IN : OP_SYRK, g.tile_sq, true, build);
   tm.done();
   return e;
 }
@@ -308,16 +384,19 @@ hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, floa
 // C = alpha * A B^T + beta * E + gamma * I, every operand m' x m' and symmetric.
 hipError_t square(const Group& g, const StepEnv& env, const void* A, const void* B, const void* E,
                   void* C, float alpha, float beta, float gamma) {
-  GemmParams p = base_params(g, env);
-  p.A = A; p.B = B; p.C = C; p.E = E;
-  p.lda = p.ldb = p.ldc = p.lde = g.Mp;
-  p.sA = p.sB = p.sC = p.sE = g.stride_sq;
-  p.M = p.N = p.K = static_cast<int32_t>(g.Mp);
-  p.alpha = alpha; p.beta = beta; p.gamma = gamma;
-  set_sym_tiles(p, g.Mp, g.tile_sq);
-  const double cnt = static_cast<double>(p.count);
-  StageTimer tm(env.ctx, env.st, ST_SQUARE, g.m, g.n, p.count, cnt * g.m * g.m * g.m, 0.0);
-  const hipError_t e = launch_gemm(OP_SYM, env.f32, g.tile_sq, p, env.st);
+  auto build = [&](int cfg) {
+    GemmParams p = base_params(g, env);
+    p.A = A; p.B = B; p.C = C; p.E = E;
+    p.lda = p.ldb = p.ldc = p.lde = g.Mp;
+    p.sA = p.sB = p.sC = p.sE = g.stride_sq;
+    p.M = p.N = p.K = static_cast<int32_t>(g.Mp);
+    p.alpha = alpha; p.beta = beta; p.gamma = gamma;
+    set_sym_tiles(p, g.Mp, cfg);
+    return p;
+  };
+  const double cnt = static_cast<double>(g.members.size());
+  StageTimer tm(env.ctx, env.st, ST_SQUARE, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.m, 0.0);
+  const hipError_t e = run_stage(env, g, OP_SYM, g.tile_sq, true, build);
   tm.done();
   return e;
 }
@@ -327,28 +406,30 @@ hipError_t square(const Group& g, const StepEnv& env, const void* A, const void*
 hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* XT, void* X,
                  void* XTout, float alpha, float beta, float oscale, bool use_e, bool update,
                  const MatDesc* table) {
-  GemmParams p = base_params(g, env);
-  p.A = Q; p.B = XT; p.C = X; p.C2 = XTout; p.E = use_e ? XT : nullptr;
-  p.e_trans = 1;
-  p.lda = g.Mp; p.ldb = g.Mp; p.ldc = g.Np; p.ldc2 = g.Mp; p.lde = g.Mp;
-  p.sA = g.stride_sq; p.sB = g.stride_x; p.sC = g.stride_x; p.sC2 = g.stride_x; p.sE = g.stride_x;
-  p.M = static_cast<int32_t>(g.Mp); p.N = static_cast<int32_t>(g.Np); p.K = static_cast<int32_t>(g.Mp);
-  p.alpha = alpha; p.beta = beta; p.oscale = oscale;
-  const int t = g.tile_ap;
-  p.tiles_m = static_cast<int32_t>((g.Mp + tile_bm(t) - 1) / tile_bm(t));
-  p.tiles_n = static_cast<int32_t>((g.Np + tile_bn(t) - 1) / tile_bn(t));
-  p.tiles = p.tiles_m * p.tiles_n;
-  if (update) {
-    p.table = table;
-    p.lr = env.hp->lr;
-    p.wd = env.hp->weight_decay;
-    p.w_bf16 = env.hp->w_dtype == MUON_BF16;
-  }
-  const double cnt = static_cast<double>(p.count);
-  const double wbytes = update ? cnt * g.m * g.n * 2.0 * (p.w_bf16 ? 2.0 : 4.0) : 0.0;
-  StageTimer tm(env.ctx, env.st, update ? ST_UPDATE : ST_APPLY, g.m, g.n, p.count,
+  auto build = [&](int cfg) {
+    GemmParams p = base_params(g, env);
+    p.A = Q; p.B = XT; p.C = X; p.C2 = XTout; p.E = use_e ? XT : nullptr;
+    p.e_trans = 1;
+    p.lda = g.Mp; p.ldb = g.Mp; p.ldc = g.Np; p.ldc2 = g.Mp; p.lde = g.Mp;
+    p.sA = g.stride_sq; p.sB = g.stride_x; p.sC = g.stride_x; p.sC2 = g.stride_x; p.sE = g.stride_x;
+    p.M = static_cast<int32_t>(g.Mp); p.N = static_cast<int32_t>(g.Np); p.K = static_cast<int32_t>(g.Mp);
+    p.alpha = alpha; p.beta = beta; p.oscale = oscale;
+    p.tiles_m = static_cast<int32_t>((g.Mp + tile_bm(cfg) - 1) / tile_bm(cfg));
+    p.tiles_n = static_cast<int32_t>((g.Np + tile_bn(cfg) - 1) / tile_bn(cfg));
+    p.tiles = p.tiles_m * p.tiles_n;
+    if (update) {
+      p.table = table;
+      p.lr = env.hp->lr;
+      p.wd = env.hp->weight_decay;
+      p.w_bf16 = env.hp->w_dtype == MUON_BF16;
+    }
+    return p;
+  };
+  const double cnt = static_cast<double>(g.members.size());
+  const double wbytes = update ? cnt * g.m * g.n * 2.0 * (env.hp->w_dtype == MUON_BF16 ? 2.0 : 4.0) : 0.0;
+  StageTimer tm(env.ctx, env.st, update ? ST_UPDATE : ST_APPLY, g.m, g.n, static_cast<int>(cnt),
                 cnt * 2.0 * g.m * g.m * g.n, wbytes);
-  const hipError_t e = launch_gemm(update ? OP_UPDATE : OP_APPLY, env.f32, t, p, env.st);
+  const hipError_t e = run_stage(env, g, update ? OP_UPDATE : OP_APPLY, g.tile_ap, false, build);
   tm.done();
   return e;
 }
@@ -608,7 +689,18 @@ int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon
     out->m = g.m;
     out->n = g.n;
     out->group = plan.group_of[index];
-    out->tile = tile_bm(g.tile_ap);
+    out->tile_sym = g.tile_sq;
+    out->tile_apply = g.tile_ap;
+    out->reserved = 0;
+    if (!(ctx->flags & MUON_FLAG_MODEL_ONLY)) {
+      const int f32 = hp->ns_dtype == MUON_F32 ? 1 : 0;
+      const int cnt = static_cast<int>(g.members.size());
+      std::lock_guard<std::mutex> lk(g_tune_mu);
+      auto a = g_tuned.find(std::make_tuple(ctx->device, static_cast<int>(OP_SYM), f32, g.Mp, g.Mp, cnt));
+      if (a != g_tuned.end()) out->tile_sym = a->second;
+      auto b = g_tuned.find(std::make_tuple(ctx->device, static_cast<int>(OP_APPLY), f32, g.Mp, g.Np, cnt));
+      if (b != g_tuned.end()) out->tile_apply = b->second;
+    }
     out->dense_flops = dense_flops(g.m, g.n, g.mode, *hp);
     out->kernel_flops = kernel_flops(g.m, g.n, g.mode, *hp);
     return MUON_OK;
@@ -709,12 +801,14 @@ int muon_profile_read(muon_ctx* ctx, muon_profile_entry* out, int capacity, int*
 
 int muon_destroy(muon_ctx* ctx) {
   if (!ctx) return MUON_OK;
-  if (ctx->device >= 0 && !ctx->event_pool.empty()) {
+  if (ctx->device >= 0) {
     DeviceGuard dg(ctx->device);
     for (auto& ev : ctx->event_pool) {
       (void)hipEventDestroy(ev.first);
       (void)hipEventDestroy(ev.second);
     }
+    for (hipEvent_t ev : ctx->tune_ev)
+      if (ev) (void)hipEventDestroy(ev);
   }
   delete ctx;
   return MUON_OK;

@@ -23,6 +23,10 @@
 
 #include "internal.hpp"
 
+#ifndef MUON_SCHED_GROUPS
+#define MUON_SCHED_GROUPS 1
+#endif
+
 namespace muon {
 namespace {
 
@@ -175,11 +179,13 @@ __device__ __forceinline__ void update_block(const GemmParams& p, const MatDesc&
 // general outputs or an upper-triangle walk for symmetric ones.
 template <bool SYM>
 __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& tn) {
-  int t = blockIdx.x;
+  // Workgroups are dealt round-robin to the 8 XCDs (workgroup i runs on XCD i % 8); give
+  // each XCD a contiguous run of logical tiles so neighbouring tiles (shared operand
+  // panels) share one L2. XCD x holds nwg/8 tiles, plus one if x < nwg % 8.
+  const int i = blockIdx.x;
   const int nwg = gridDim.x;
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous run of
-  // logical tiles so neighbouring tiles (shared operand panels) share one L2.
-  if ((nwg & 7) == 0) t = (t & 7) * (nwg >> 3) + (t >> 3);
+  const int x = i & 7, q = nwg >> 3, r = nwg & 7;
+  int t = x * q + min(x, r) + (i >> 3);
   if constexpr (SYM) {
     int row = 0;
     int len = p.tiles_n;
@@ -198,7 +204,208 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
   }
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int PF, bool SYM, int EPI>
+// Epilogue shared by both kernels: per 32x32 block a lane holds column c and rows
+// r0..r0+3 for q = 0..3 (acc[i][j][4q + e] is row r0 + e).
+template <int KIND, int BM, int BN, int WM, int WN, bool SYM, int EPI, int FM, int FN, typename TO>
+__device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][FN], int mat, int tm,
+                                         int tn, int m0, int n0, int wm0, int wn0, int lane) {
+  const float alpha = scaled(p.alpha, p.s, mat, p.alpha_spow);
+  const float beta = scaled(p.beta, p.s, mat, p.beta_spow);
+  const float gamma = p.gamma;
+  const bool has_e = p.E != nullptr;
+  const bool mirror = SYM && (tm != tn);
+
+  TO* C = nullptr;
+  TO* C2 = nullptr;
+  const TO* E = nullptr;
+  if (EPI != EPI_UPDATE) C = static_cast<TO*>(p.C) + static_cast<int64_t>(mat) * p.sC;
+  if (EPI == EPI_APPLY && p.C2 != nullptr) C2 = static_cast<TO*>(p.C2) + static_cast<int64_t>(mat) * p.sC2;
+  if (has_e) E = static_cast<const TO*>(p.E) + static_cast<int64_t>(mat) * p.sE;
+
+  MatDesc d{};
+  float decay = 1.0f;
+  if constexpr (EPI == EPI_UPDATE) {
+    d = p.table[mat];
+    decay = 1.0f - p.lr * p.wd;
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c = n0 + wn0 + j * 32 + (lane & 31);
+      float upd[4][4] = {};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r0 = m0 + wm0 + i * 32 + q * 8 + (lane >> 5) * 4;
+        // M and N are multiples of 4: rows r0..r0+3 are all in range or all out.
+        if (r0 >= p.M || c >= p.N) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][q * 4 + e];
+        if (has_e) {
+          float ev[4];
+          if (p.e_trans) {
+            load4(E + static_cast<int64_t>(c) * p.lde + r0, ev);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ev[e] = from_out(E[static_cast<int64_t>(r0 + e) * p.lde + c]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += beta * ev[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (r0 + e == c) v[e] += gamma;
+        if constexpr (EPI == EPI_STORE || EPI == EPI_APPLY) {
+          const float os = (EPI == EPI_APPLY) ? p.oscale : 1.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) C[static_cast<int64_t>(r0 + e) * p.ldc + c] = to_out<TO>(v[e] * os);
+          if (SYM && mirror) store4(C + static_cast<int64_t>(c) * p.ldc + r0, v, 1.0f);
+          if (EPI == EPI_APPLY && C2 != nullptr) store4(C2 + static_cast<int64_t>(c) * p.ldc2 + r0, v, os);
+        } else {
+          upd[q][0] = v[0]; upd[q][1] = v[1]; upd[q][2] = v[2]; upd[q][3] = v[3];
+        }
+      }
+      if constexpr (EPI == EPI_UPDATE) update_block(p, d, decay, c, m0 + wm0 + i * 32 + (lane >> 5) * 4, upd);
+    }
+  }
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Same product as gemm_kernel, with operands moved global -> LDS by the CDNA4 direct
+// loads (16 bytes per lane, lane l writing LDS bytes [16 l, 16 l + 16) of the
+// instruction's 1 KB window = 8 rows x 128 bytes). The XOR swizzle moves to the global
+// side: lane l of a window loads logical chunk (l % 8) ^ f(row). NS LDS stages form a
+// ring; slice k + NS - 1 is issued before slice k is computed, so NS - 1 slices of loads
+// are in flight and no staging registers are needed.
+template <int KIND, int BM, int BN, int WM, int WN, int NS, bool SYM, int EPI, int TAG>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(const GemmParams p) {
+  using TO = typename OutT<KIND>::T;
+  constexpr int NW = WM * WN;
+  constexpr int ES = (KIND == KIND_F32) ? 4 : 2;
+  constexpr int VEC = 16 / ES;
+  constexpr int BK = kChunks * VEC;
+  constexpr int TWM = BM / WM, TWN = BN / WN;
+  constexpr int FM = TWM / 32, FN = TWN / 32;
+  constexpr int IA = BM / (8 * NW), IB = BN / (8 * NW);   // load instructions per wave
+  static_assert(IA * 8 * NW == BM && IB * 8 * NW == BN, "rows per wave");
+  constexpr int STAGE = (BM + BN) * kChunks;               // u32x4 per stage
+  constexpr int KSTEPS = kChunks / 2;
+  constexpr int D = NS - 1;                                // slices in flight
+  static_assert(NS >= 2, "stages");
+
+  __shared__ u32x4 lds[NS * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int mat = blockIdx.y;
+
+  int tm, tn;
+  tile_coords<SYM>(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const char* Ab = static_cast<const char*>(p.A) + static_cast<int64_t>(mat) * p.sA * ES;
+  const char* Bb = static_cast<const char*>(p.B) + static_cast<int64_t>(mat) * p.sB * ES;
+
+  int64_t a_off[IA], b_off[IB];
+#pragma unroll
+  for (int j = 0; j < IA; ++j) {
+    const int row = (wave * IA + j) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const int gr = min(m0 + row, p.M - 1);
+    a_off[j] = (static_cast<int64_t>(gr) * p.lda + chunk * VEC) * ES;
+  }
+#pragma unroll
+  for (int j = 0; j < IB; ++j) {
+    const int row = (wave * IB + j) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const int gr = min(n0 + row, p.N - 1);
+    b_off[j] = (static_cast<int64_t>(gr) * p.ldb + chunk * VEC) * ES;
+  }
+
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  typedef const __attribute__((address_space(1))) void* glb_ptr;
+  auto issue = [&](int stage, int k0) {
+    const int64_t kb = static_cast<int64_t>(k0) * ES;
+    u32x4* sa = lds + stage * STAGE;
+    u32x4* sb = sa + BM * kChunks;
+#pragma unroll
+    for (int j = 0; j < IA; ++j)
+      __builtin_amdgcn_global_load_lds((glb_ptr)(Ab + a_off[j] + kb),
+                                       (lds_ptr)(sa + (wave * IA + j) * 8 * kChunks), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < IB; ++j)
+      __builtin_amdgcn_global_load_lds((glb_ptr)(Bb + b_off[j] + kb),
+                                       (lds_ptr)(sb + (wave * IB + j) * 8 * kChunks), 16, 0, 0);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int wm0 = (wave / WN) * TWM;
+  const int wn0 = (wave % WN) * TWN;
+  const int nk = p.K / BK;
+
+  u32x4 fa[2][FM], fb[2][FN];
+  auto load_frags = [&](int buf, const u32x4* la, const u32x4* lb, int kk) {
+    const int ch = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[buf][i] = la[swz(wm0 + i * 32 + (lane & 31), ch)];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[buf][j] = lb[swz(wn0 + j * 32 + (lane & 31), ch)];
+  };
+
+  // Prologue: slices 0 .. D-1 (clamped: past the end the last slice is reloaded into a
+  // stage that is never read, so every iteration issues the same number of loads).
+#pragma unroll
+  for (int s0 = 0; s0 < D; ++s0) issue(s0, min(s0, nk - 1) * BK);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<(D - 1) * (IA + IB)>();  // this wave's part of slice kt has landed
+    __builtin_amdgcn_s_barrier();         // ... and every wave's; slice kt-1's stage is free
+    issue((kt + D) % NS, min(kt + D, nk - 1) * BK);
+    const u32x4* la = lds + (kt % NS) * STAGE;
+    const u32x4* lb = la + BM * kChunks;
+    load_frags(0, la, lb, 0);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (kk + 1 < KSTEPS) load_frags((kk + 1) & 1, la, lb, kk + 1);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mma<KIND>(acc[i][j], fa[kk & 1][i], fb[kk & 1][j]);
+    }
+#if MUON_SCHED_GROUPS
+    // Order the slice as R0 R1 M0 R2 M1 R3 M2 M3 (Rk: LDS fragment reads of k-step k,
+    // Mk: its MFMAs), so each k-step's reads are in flight during the previous MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+    for (int kk = 1; kk < KSTEPS; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (KIND == KIND_F32 ? 4 : 1) * FM * FN, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, (KIND == KIND_F32 ? 4 : 1) * FM * FN, 0);
+#endif
+  }
+  wait_vmcnt<0>();
+
+  epilogue<KIND, BM, BN, WM, WN, SYM, EPI, FM, FN, TO>(p, acc, mat, tm, tn, m0, n0, wm0, wn0, lane);
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, int PF, bool SYM, int EPI, int TAG>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmParams p) {
   static_assert(PF == 1 || PF == 2, "prefetch distance");
   using TO = typename OutT<KIND>::T;
@@ -349,89 +556,48 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmParams p) 
     }
   }
 
-  // ---- epilogue: per 32x32 block a lane holds column c, rows r0..r0+3 for q = 0..3 ----
-  const float alpha = scaled(p.alpha, p.s, mat, p.alpha_spow);
-  const float beta = scaled(p.beta, p.s, mat, p.beta_spow);
-  const float gamma = p.gamma;
-  const bool has_e = p.E != nullptr;
-  const bool mirror = SYM && (tm != tn);
-
-  TO* C = nullptr;
-  TO* C2 = nullptr;
-  const TO* E = nullptr;
-  if (EPI != EPI_UPDATE) C = static_cast<TO*>(p.C) + static_cast<int64_t>(mat) * p.sC;
-  if (EPI == EPI_APPLY && p.C2 != nullptr) C2 = static_cast<TO*>(p.C2) + static_cast<int64_t>(mat) * p.sC2;
-  if (has_e) E = static_cast<const TO*>(p.E) + static_cast<int64_t>(mat) * p.sE;
-
-  MatDesc d{};
-  float decay = 1.0f;
-  if constexpr (EPI == EPI_UPDATE) {
-    d = p.table[mat];
-    decay = 1.0f - p.lr * p.wd;
-  }
-
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int c = n0 + wn0 + j * 32 + (lane & 31);
-      float upd[4][4] = {};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r0 = m0 + wm0 + i * 32 + q * 8 + (lane >> 5) * 4;
-        // M and N are multiples of 4: rows r0..r0+3 are all in range or all out.
-        if (r0 >= p.M || c >= p.N) continue;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][q * 4 + e];
-        if (has_e) {
-          float ev[4];
-          if (p.e_trans) {
-            load4(E + static_cast<int64_t>(c) * p.lde + r0, ev);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ev[e] = from_out(E[static_cast<int64_t>(r0 + e) * p.lde + c]);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += beta * ev[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (r0 + e == c) v[e] += gamma;
-        if constexpr (EPI == EPI_STORE || EPI == EPI_APPLY) {
-          const float os = (EPI == EPI_APPLY) ? p.oscale : 1.0f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) C[static_cast<int64_t>(r0 + e) * p.ldc + c] = to_out<TO>(v[e] * os);
-          if (SYM && mirror) store4(C + static_cast<int64_t>(c) * p.ldc + r0, v, 1.0f);
-          if (EPI == EPI_APPLY && C2 != nullptr) store4(C2 + static_cast<int64_t>(c) * p.ldc2 + r0, v, os);
-        } else {
-          upd[q][0] = v[0]; upd[q][1] = v[1]; upd[q][2] = v[2]; upd[q][3] = v[3];
-        }
-      }
-      if constexpr (EPI == EPI_UPDATE) update_block(p, d, decay, c, m0 + wm0 + i * 32 + (lane >> 5) * 4, upd);
-    }
-  }
+  epilogue<KIND, BM, BN, WM, WN, SYM, EPI, FM, FN, TO>(p, acc, mat, tm, tn, m0, n0, wm0, wn0, lane);
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int PF, bool SYM, int EPI>
+// TAG only gives otherwise identical instantiations their own symbol (profiles tell the
+// Gram product of the iterate from the m' x m' products).
+template <int KIND, int BM, int BN, int WM, int WN, int PF, bool SYM, int EPI, int TAG>
 hipError_t launch_shape(const GemmParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, PF, SYM, EPI>), dim3(p.tiles, p.count),
+  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, PF, SYM, EPI, TAG>), dim3(p.tiles, p.count),
                      dim3(64 * WM * WN), 0, st, p);
   return hipGetLastError();
 }
 
-template <int KIND, bool SYM, int EPI>
+template <int KIND, int BM, int BN, int WM, int WN, int NS, bool SYM, int EPI, int TAG>
+hipError_t launch_dma(const GemmParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_dma_kernel<KIND, BM, BN, WM, WN, NS, SYM, EPI, TAG>), dim3(p.tiles, p.count),
+                     dim3(64 * WM * WN), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int KIND, bool SYM, int EPI, int TAG = 0>
 hipError_t launch_tile(int cfg, const GemmParams& p, hipStream_t st) {
   switch (cfg) {
     // 64 and 128 tiles keep two slices of loads in flight (few workgroups per CU must
     // hide the load latency themselves); the 8-wave 256 tiles keep one.
-    case TILE_64: return launch_shape<KIND, 64, 64, 2, 2, 2, SYM, EPI>(p, st);
-    case TILE_128: return launch_shape<KIND, 128, 128, 2, 2, 2, SYM, EPI>(p, st);
+    case TILE_64: return launch_shape<KIND, 64, 64, 2, 2, 2, SYM, EPI, TAG>(p, st);
+    case TILE_128: return launch_shape<KIND, 128, 128, 2, 2, 2, SYM, EPI, TAG>(p, st);
     case TILE_256:  // 8 waves (2 per SIMD), wave tile 128 x 64
-      if constexpr (KIND != KIND_F32) return launch_shape<KIND, 256, 256, 2, 4, 1, SYM, EPI>(p, st);
+      if constexpr (KIND != KIND_F32) return launch_shape<KIND, 256, 256, 2, 4, 1, SYM, EPI, TAG>(p, st);
       return hipErrorInvalidValue;
     case TILE_256x128:  // 8 waves, wave tile 64 x 64
-      if constexpr (!SYM && KIND != KIND_F32) return launch_shape<KIND, 256, 128, 4, 2, 1, SYM, EPI>(p, st);
+      if constexpr (!SYM && KIND != KIND_F32) return launch_shape<KIND, 256, 128, 4, 2, 1, SYM, EPI, TAG>(p, st);
+      return hipErrorInvalidValue;
+    case TILE_64_DMA: return launch_dma<KIND, 64, 64, 2, 2, 4, SYM, EPI, TAG>(p, st);
+    case TILE_128_DMA: return launch_dma<KIND, 128, 128, 2, 2, 4, SYM, EPI, TAG>(p, st);
+    case TILE_256x128_DMA:
+      if constexpr (!SYM && KIND != KIND_F32) return launch_dma<KIND, 256, 128, 4, 2, 3, SYM, EPI, TAG>(p, st);
+      return hipErrorInvalidValue;
+    case TILE_256_DMA:
+      if constexpr (KIND != KIND_F32) return launch_dma<KIND, 256, 256, 2, 4, 2, SYM, EPI, TAG>(p, st);
+      return hipErrorInvalidValue;
+    case TILE_256_DMA4:
+      if constexpr (KIND != KIND_F32) return launch_dma<KIND, 256, 256, 2, 2, 2, SYM, EPI, TAG>(p, st);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
@@ -444,6 +610,7 @@ hipError_t launch_gemm(GemmOp op, bool ns_f32, int cfg, const GemmParams& p, hip
   if (ns_f32) {
     switch (op) {
       case OP_SYRK_IN:
+      case OP_SYRK: return launch_tile<KIND_F32, true, EPI_STORE, 1>(cfg, p, st);
       case OP_SYM: return launch_tile<KIND_F32, true, EPI_STORE>(cfg, p, st);
       case OP_APPLY: return launch_tile<KIND_F32, false, EPI_APPLY>(cfg, p, st);
       case OP_UPDATE: return launch_tile<KIND_F32, false, EPI_UPDATE>(cfg, p, st);
@@ -451,6 +618,7 @@ hipError_t launch_gemm(GemmOp op, bool ns_f32, int cfg, const GemmParams& p, hip
   } else {
     switch (op) {
       case OP_SYRK_IN: return launch_tile<KIND_BF16, true, EPI_STORE>(cfg, p, st);
+      case OP_SYRK: return launch_tile<KIND_F16, true, EPI_STORE, 1>(cfg, p, st);
       case OP_SYM: return launch_tile<KIND_F16, true, EPI_STORE>(cfg, p, st);
       case OP_APPLY: return launch_tile<KIND_F16, false, EPI_APPLY>(cfg, p, st);
       case OP_UPDATE: return launch_tile<KIND_F16, false, EPI_UPDATE>(cfg, p, st);

@@ -54,18 +54,32 @@ enum GemmOp : int {
   OP_SYM = 1,      // A B^T with symmetric output (fp16 / fp32 operands)
   OP_APPLY = 2,    // A B^T, general output, X in both layouts
   OP_UPDATE = 3,   // A B^T, epilogue updates W
+  OP_SYRK = 4,     // X X^T on the fp16 / fp32 iterate (same kernel as OP_SYM, own symbol)
 };
 
 // Workgroup tile configurations (4 waves each). Symmetric-output stages need BM == BN.
+// Configurations 0-3 stage operands through registers; 4-8 use the CDNA4 direct
+// global -> LDS loads with a multi-stage LDS ring.
 enum TileCfg : int {
-  TILE_64 = 0,       // 64 x 64, wave tile 32 x 32
-  TILE_128 = 1,      // 128 x 128, wave tile 64 x 64
-  TILE_256x128 = 2,  // 256 x 128, wave tile 128 x 64
-  TILE_256 = 3,      // 256 x 256, wave tile 128 x 128
-  TILE_COUNT = 4
+  TILE_64 = 0,           // 64 x 64, 4 waves, wave tile 32 x 32
+  TILE_128 = 1,          // 128 x 128, 4 waves, wave tile 64 x 64
+  TILE_256x128 = 2,      // 256 x 128, 8 waves, wave tile 64 x 64
+  TILE_256 = 3,          // 256 x 256, 8 waves, wave tile 128 x 64
+  TILE_64_DMA = 4,       // as TILE_64, 4 LDS stages
+  TILE_128_DMA = 5,      // as TILE_128, 4 LDS stages
+  TILE_256x128_DMA = 6,  // as TILE_256x128, 3 LDS stages
+  TILE_256_DMA = 7,      // as TILE_256, 2 LDS stages
+  TILE_256_DMA4 = 8,     // 256 x 256, 4 waves, wave tile 128 x 128, 2 LDS stages
+  TILE_COUNT = 9
 };
-inline int tile_bm(int cfg) { return cfg == TILE_64 ? 64 : cfg == TILE_128 ? 128 : 256; }
-inline int tile_bn(int cfg) { return cfg == TILE_64 ? 64 : cfg == TILE_256 ? 256 : 128; }
+inline int tile_bm(int cfg) {
+  static const int bm[TILE_COUNT] = {64, 128, 256, 256, 64, 128, 256, 256, 256};
+  return bm[cfg];
+}
+inline int tile_bn(int cfg) {
+  static const int bn[TILE_COUNT] = {64, 128, 128, 256, 64, 128, 128, 256, 256};
+  return bn[cfg];
+}
 
 // Launch one batched GEMM stage. ns_f32: fp32 kernels, else bf16/fp16 kernels.
 hipError_t launch_gemm(GemmOp op, bool ns_f32, int cfg, const GemmParams& p, hipStream_t st);

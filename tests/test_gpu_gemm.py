@@ -56,8 +56,13 @@ def check_elems(got, ref, K, u_out):
     assert not bad.any(), (np.argwhere(bad)[:5], got[bad][:5], ref[bad][:5])
 
 
-# tile configurations: 0 = 64x64, 1 = 128x128, 2 = 256x128 (apply only), 3 = 256x256
-@pytest.mark.parametrize("tile", [0, 1, 3])
+# tile configurations: 0 = 64x64, 1 = 128x128, 2 = 256x128 (apply only), 3 = 256x256;
+# 4-7: the same tiles with direct global -> LDS loads
+SYM_TILES = [0, 1, 3, 4, 5, 7, 8]
+ALL_TILES = [0, 1, 2, 3, 4, 5, 6, 7, 8]
+
+
+@pytest.mark.parametrize("tile", SYM_TILES)
 @pytest.mark.parametrize("M,K", [(64, 64), (192, 320), (256, 1024), (384, 128), (640, 192)])
 def test_syrk_bf16(B, ctx, tile, M, K):
     rng = np.random.default_rng(M * 31 + K + tile)
@@ -72,7 +77,7 @@ def test_syrk_bf16(B, ctx, tile, M, K):
     assert np.array_equal(got, got.T)  # mirrored store: exactly symmetric
 
 
-@pytest.mark.parametrize("tile", [0, 1])
+@pytest.mark.parametrize("tile", [0, 1, 4, 5])
 @pytest.mark.parametrize("M,K", [(128, 256), (320, 192)])
 def test_syrk_f32(B, ctx, tile, M, K):
     rng = np.random.default_rng(M + K + tile)
@@ -86,10 +91,10 @@ def test_syrk_f32(B, ctx, tile, M, K):
     assert np.array_equal(got, got.T)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 3])
+@pytest.mark.parametrize("tile", SYM_TILES)
 @pytest.mark.parametrize("ns,dt,u", [("bf16", torch.float16, 2.0 ** -11), ("f32", torch.float32, 2.0 ** -24)])
 def test_square_poly(B, ctx, tile, ns, dt, u):
-    if ns == "f32" and tile == 3:
+    if ns == "f32" and tile in (3, 7, 8):
         pytest.skip("256x256 tiles are not built for fp32")
     M = 576
     rng = np.random.default_rng(tile)
@@ -107,7 +112,7 @@ def test_square_poly(B, ctx, tile, ns, dt, u):
     assert np.array_equal(got, got.T)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 3])
+@pytest.mark.parametrize("tile", SYM_TILES)
 @pytest.mark.parametrize("M,K", [(128, 576), (320, 192)])
 def test_sym_long_fp16(B, ctx, tile, M, K):
     """kind 1 with A = B = X (M x K, K != M): the Gram product of the fp16 iterate."""
@@ -122,7 +127,7 @@ def test_sym_long_fp16(B, ctx, tile, M, K):
     assert np.array_equal(got, got.T)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+@pytest.mark.parametrize("tile", ALL_TILES)
 @pytest.mark.parametrize("M,N,K", [(128, 320, 192), (256, 1024, 256), (64, 64, 64), (384, 704, 320)])
 def test_apply_fp16(B, ctx, tile, M, N, K):
     """kind 2: v = alpha A B^T + beta E^T; C = oscale v and C2 = oscale v^T (fp16)."""
@@ -143,7 +148,7 @@ def test_apply_fp16(B, ctx, tile, M, N, K):
     assert rel(got, ref) < 1e-3
 
 
-@pytest.mark.parametrize("tile", [0, 1])
+@pytest.mark.parametrize("tile", [0, 1, 4, 5])
 def test_apply_f32(B, ctx, tile):
     M, N, K = 192, 448, 128
     rng = np.random.default_rng(tile + 5)

@@ -146,6 +146,20 @@ def test_bf16_2560x9728_full_size(B, ctx):
     assert e_gram <= 2e-2 and e_plain <= 2e-2
 
 
+@pytest.mark.parametrize("mode", ["gram", "plain"])
+def test_bf16_split_k(B, ctx, mode):
+    """Single mid-size matrices: too few tiles for the GPU, so the symmetric stages split K
+    over several workgroups (last-arriver reduction)."""
+    w = wl.custom("splitk", [(512, 4096), (2048, 384)], structure="lowrank", rank=16, wid=210)
+    check_step(B, ctx, w, mode=mode)
+
+
+def test_fp32_split_k(B, ctx):
+    w = wl.custom("splitk32", [(256, 4096)], dtype="f32", wid=211)
+    check_step(B, ctx, w, mode="gram")
+    check_step(B, ctx, w, mode="plain")
+
+
 def test_small_batch_832_full(B, ctx):
     w = wl.WORKLOADS["small_batch_832"]
     check_step(B, ctx, w, mode="gram", gpu_mode="auto")

@@ -326,12 +326,12 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
     if (!found) {
       std::vector<int> cands;
       if (env.f32) {
-        cands = {TILE_64, TILE_128, TILE_64_DMA, TILE_128_DMA};
+        cands = {TILE_64, TILE_128, TILE_64_DMA, TILE_128_DMA, TILE_128_DMA_K2};
       } else if (sym) {
-        cands = {TILE_64, TILE_128, TILE_128_DMA};
+        cands = {TILE_64, TILE_128, TILE_128_DMA, TILE_128_DMA_K2};
         if (g.Mp >= 512) cands.push_back(TILE_256_DMA);
       } else {
-        cands = {TILE_64, TILE_128};
+        cands = {TILE_64, TILE_128, TILE_128_DMA_K2};
         if (g.Mp >= 256) {
           cands.push_back(TILE_256x128_DMA);
           cands.push_back(TILE_256_DMA);

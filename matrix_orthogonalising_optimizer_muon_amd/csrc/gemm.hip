@@ -124,54 +124,50 @@ __device__ __forceinline__ void store4(T* p, const float (&v)[4], float scale) {
   }
 }
 
-// W <- W*decay - lr*O for one lane's 16 values of a 32x32 block: rows rb + 8q + e
-// (q, e = 0..3) of column c in canonical orientation. All loads are issued before any
-// store; a transposed W holds the 4 rows of each q contiguously (16-byte accesses when
-// aligned).
-__device__ __forceinline__ void update_block(const GemmParams& p, const MatDesc& d, float decay, int c,
-                                             int rb, const float (&o)[4][4]) {
-  if (c >= p.Nvalid) return;
-  float w[4][4];
-  int64_t idx[4][4];
-  bool ok[4][4];
-  const bool vec = d.transposed && !p.w_bf16 && (d.cols % 4) == 0 &&
-                   (reinterpret_cast<uintptr_t>(d.W) % 16) == 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r0 = rb + q * 8;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + e;
-      ok[q][e] = r < p.Mvalid;
-      idx[q][e] = d.transposed ? static_cast<int64_t>(c) * d.cols + r : static_cast<int64_t>(r) * d.cols + c;
-    }
-    if (vec && r0 + 3 < p.Mvalid) {
-      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(d.W) + idx[q][0]);
-      w[q][0] = x.x; w[q][1] = x.y; w[q][2] = x.z; w[q][3] = x.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (!ok[q][e]) { w[q][e] = 0.0f; continue; }
-        w[q][e] = p.w_bf16 ? bf16_to_f32(static_cast<const unsigned short*>(d.W)[idx[q][e]])
-                           : static_cast<const float*>(d.W)[idx[q][e]];
-      }
-    }
+// W element (r, c) of the canonical orientation through the descriptor: a transposed W
+// holds the canonical column contiguously, so the 4 rows r0..r0+3 of a block are one
+// 16-byte access when W is fp32 and aligned.
+__device__ __forceinline__ int64_t w_index(const MatDesc& d, int r, int c) {
+  return d.transposed ? static_cast<int64_t>(c) * d.cols + r : static_cast<int64_t>(r) * d.cols + c;
+}
+__device__ __forceinline__ bool w_vec(const GemmParams& p, const MatDesc& d) {
+  return d.transposed && !p.w_bf16 && (d.cols % 4) == 0 && (reinterpret_cast<uintptr_t>(d.W) % 16) == 0;
+}
+// Load W at rows r0..r0+3 of column c (zero outside the valid region).
+__device__ __forceinline__ void w_load4(const GemmParams& p, const MatDesc& d, bool vec, int r0, int c,
+                                        float* w) {
+  const bool cin = c < p.Nvalid;
+  if (vec && cin && r0 + 3 < p.Mvalid) {
+    const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(d.W) + w_index(d, r0, c));
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    return;
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float n[4];
+  for (int e = 0; e < 4; ++e) {
+    const bool ok = cin && r0 + e < p.Mvalid;
+    const int64_t wi = ok ? w_index(d, r0 + e, c) : 0;
+    w[e] = !ok ? 0.0f
+               : (p.w_bf16 ? bf16_to_f32(static_cast<const unsigned short*>(d.W)[wi])
+                           : static_cast<const float*>(d.W)[wi]);
+  }
+}
+// W <- W*decay - lr*o at rows r0..r0+3 of column c, given the loaded w.
+__device__ __forceinline__ void w_store4(const GemmParams& p, const MatDesc& d, bool vec, float decay,
+                                         int r0, int c, const float* w, const float (&o)[4]) {
+  if (c >= p.Nvalid) return;
+  float n[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) n[e] = w[q][e] * decay - p.lr * o[q][e];
-    if (vec && rb + q * 8 + 3 < p.Mvalid) {
-      *reinterpret_cast<float4*>(static_cast<float*>(d.W) + idx[q][0]) = make_float4(n[0], n[1], n[2], n[3]);
-    } else {
+  for (int e = 0; e < 4; ++e) n[e] = w[e] * decay - p.lr * o[e];
+  if (vec && r0 + 3 < p.Mvalid) {
+    *reinterpret_cast<float4*>(static_cast<float*>(d.W) + w_index(d, r0, c)) = make_float4(n[0], n[1], n[2], n[3]);
+    return;
+  }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (!ok[q][e]) continue;
-        if (p.w_bf16) static_cast<unsigned short*>(d.W)[idx[q][e]] = f32_to_bf16(n[e]);
-        else static_cast<float*>(d.W)[idx[q][e]] = n[e];
-      }
-    }
+  for (int e = 0; e < 4; ++e) {
+    if (r0 + e >= p.Mvalid) continue;
+    const int64_t wi = w_index(d, r0 + e, c);
+    if (p.w_bf16) static_cast<unsigned short*>(d.W)[wi] = f32_to_bf16(n[e]);
+    else static_cast<float*>(d.W)[wi] = n[e];
   }
 }
 
@@ -206,6 +202,9 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
 
 // Epilogue shared by both kernels: per 32x32 block a lane holds column c and rows
 // r0..r0+3 for q = 0..3 (acc[i][j][4q + e] is row r0 + e).
+// The W update loads every W value of a chunk of block rows before computing and storing
+// them, so a wave pays one memory round trip per chunk instead of one per block; a chunk
+// holds at most 64 (8-wave tiles: 32) W values per lane to stay within the register file.
 template <int KIND, int BM, int BN, int WM, int WN, bool SYM, int EPI, int FM, int FN, typename TO>
 __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][FN], int mat, int tm,
                                          int tn, int m0, int n0, int wm0, int wn0, int lane) {
@@ -222,52 +221,82 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
   if (EPI == EPI_APPLY && p.C2 != nullptr) C2 = static_cast<TO*>(p.C2) + static_cast<int64_t>(mat) * p.sC2;
   if (has_e) E = static_cast<const TO*>(p.E) + static_cast<int64_t>(mat) * p.sE;
 
-  MatDesc d{};
-  float decay = 1.0f;
-  if constexpr (EPI == EPI_UPDATE) {
-    d = p.table[mat];
-    decay = 1.0f - p.lr * p.wd;
-  }
+  // v = alpha acc + beta E + gamma I for rows r0..r0+3 of column c of block (i, j).
+  auto value = [&](int i, int j, int q, int r0, int c, float (&v)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][q * 4 + e];
+    if (has_e) {
+      float ev[4];
+      if (p.e_trans) {
+        load4(E + static_cast<int64_t>(c) * p.lde + r0, ev);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ev[e] = from_out(E[static_cast<int64_t>(r0 + e) * p.lde + c]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += beta * ev[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (r0 + e == c) v[e] += gamma;
+  };
 
+  if constexpr (EPI == EPI_UPDATE) {
+    const MatDesc d = p.table[mat];
+    const float decay = 1.0f - p.lr * p.wd;
+    const bool vec = w_vec(p, d);
+    constexpr int WB = (WM * WN >= 8) ? 32 : 64;  // W values per lane per chunk
+    constexpr int IG = (FN * 16 >= WB) ? 1 : ((WB / (FN * 16)) < FM ? WB / (FN * 16) : FM);
+    static_assert(FM % IG == 0, "update chunk");
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i0 = 0; i0 < FM; i0 += IG) {
+      float w[IG][FN][16];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int c = n0 + wn0 + j * 32 + (lane & 31);
-      float upd[4][4] = {};
+      for (int ii = 0; ii < IG; ++ii)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r0 = m0 + wm0 + i * 32 + q * 8 + (lane >> 5) * 4;
-        // M and N are multiples of 4: rows r0..r0+3 are all in range or all out.
-        if (r0 >= p.M || c >= p.N) continue;
-        float v[4];
+        for (int j = 0; j < FN; ++j) {
+          const int c = n0 + wn0 + j * 32 + (lane & 31);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][q * 4 + e];
-        if (has_e) {
-          float ev[4];
-          if (p.e_trans) {
-            load4(E + static_cast<int64_t>(c) * p.lde + r0, ev);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ev[e] = from_out(E[static_cast<int64_t>(r0 + e) * p.lde + c]);
+          for (int q = 0; q < 4; ++q) {
+            const int r0 = m0 + wm0 + (i0 + ii) * 32 + q * 8 + (lane >> 5) * 4;
+            w_load4(p, d, vec, r0, c, &w[ii][j][4 * q]);
           }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += beta * ev[e];
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (r0 + e == c) v[e] += gamma;
-        if constexpr (EPI == EPI_STORE || EPI == EPI_APPLY) {
+      for (int ii = 0; ii < IG; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int c = n0 + wn0 + j * 32 + (lane & 31);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r0 = m0 + wm0 + (i0 + ii) * 32 + q * 8 + (lane >> 5) * 4;
+            if (r0 >= p.M || c >= p.N) continue;
+            float v[4];
+            value(i0 + ii, j, q, r0, c, v);
+            w_store4(p, d, vec, decay, r0, c, &w[ii][j][4 * q], v);
+          }
+        }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int c = n0 + wn0 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r0 = m0 + wm0 + i * 32 + q * 8 + (lane >> 5) * 4;
+          // M and N are multiples of 4: rows r0..r0+3 are all in range or all out.
+          if (r0 >= p.M || c >= p.N) continue;
+          float v[4];
+          value(i, j, q, r0, c, v);
           const float os = (EPI == EPI_APPLY) ? p.oscale : 1.0f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) C[static_cast<int64_t>(r0 + e) * p.ldc + c] = to_out<TO>(v[e] * os);
           if (SYM && mirror) store4(C + static_cast<int64_t>(c) * p.ldc + r0, v, 1.0f);
           if (EPI == EPI_APPLY && C2 != nullptr) store4(C2 + static_cast<int64_t>(c) * p.ldc2 + r0, v, os);
-        } else {
-          upd[q][0] = v[0]; upd[q][1] = v[1]; upd[q][2] = v[2]; upd[q][3] = v[3];
         }
       }
-      if constexpr (EPI == EPI_UPDATE) update_block(p, d, decay, c, m0 + wm0 + i * 32 + (lane >> 5) * 4, upd);
     }
   }
 }
@@ -286,10 +315,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // side: lane l of a window loads logical chunk (l % 8) ^ f(row). NS LDS stages form a
 // ring; slice k + NS - 1 is issued before slice k is computed, so NS - 1 slices of loads
 // are in flight and no staging registers are needed.
-template <int KIND, int BM, int BN, int WM, int WN, int NS, bool SYM, int EPI, int TAG>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(const GemmParams p) {
+template <int KIND, int BM, int BN, int WM, int WN, int NS, int KS, bool SYM, int EPI, int TAG>
+__global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmParams p) {
   using TO = typename OutT<KIND>::T;
-  constexpr int NW = WM * WN;
+  constexpr int NWC = WM * WN;                             // waves per k-group (one tile each)
+  constexpr int NW = NWC * KS;                             // waves
   constexpr int ES = (KIND == KIND_F32) ? 4 : 2;
   constexpr int VEC = 16 / ES;
   constexpr int BK = kChunks * VEC;
@@ -299,14 +329,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(const GemmParams
   static_assert(IA * 8 * NW == BM && IB * 8 * NW == BN, "rows per wave");
   constexpr int STAGE = (BM + BN) * kChunks;               // u32x4 per stage
   constexpr int KSTEPS = kChunks / 2;
+  constexpr int KL = KSTEPS / KS;                          // k-steps per wave per slice
   constexpr int D = NS - 1;                                // slices in flight
-  static_assert(NS >= 2, "stages");
+  static_assert(NS >= 2 && (KS == 1 || KS == 2), "stages / k-groups");
+  static_assert(KS == 1 || BM * BN * 4 <= NS * STAGE * 16, "k-group reduction fits in LDS");
 
   __shared__ u32x4 lds[NS * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int kgrp = wave / NWC;     // which k-steps of every slice this wave computes
+  const int wloc = wave % NWC;     // which wave tile of the output
   const int mat = blockIdx.y;
 
   int tm, tn;
@@ -356,9 +390,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(const GemmParams
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int wm0 = (wave / WN) * TWM;
-  const int wn0 = (wave % WN) * TWN;
+  const int wm0 = (wloc / WN) * TWM;
+  const int wn0 = (wloc % WN) * TWN;
   const int nk = p.K / BK;
+  const int kk0 = kgrp * KL;
 
   u32x4 fa[2][FM], fb[2][FN];
   auto load_frags = [&](int buf, const u32x4* la, const u32x4* lb, int kk) {
@@ -379,21 +414,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(const GemmParams
     issue((kt + D) % NS, min(kt + D, nk - 1) * BK);
     const u32x4* la = lds + (kt % NS) * STAGE;
     const u32x4* lb = la + BM * kChunks;
-    load_frags(0, la, lb, 0);
+    load_frags(0, la, lb, kk0);
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      if (kk + 1 < KSTEPS) load_frags((kk + 1) & 1, la, lb, kk + 1);
+    for (int kl = 0; kl < KL; ++kl) {
+      if (kl + 1 < KL) load_frags((kl + 1) & 1, la, lb, kk0 + kl + 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) mma<KIND>(acc[i][j], fa[kk & 1][i], fb[kk & 1][j]);
+        for (int j = 0; j < FN; ++j) mma<KIND>(acc[i][j], fa[kl & 1][i], fb[kl & 1][j]);
     }
 #if MUON_SCHED_GROUPS
-    // Order the slice as R0 R1 M0 R2 M1 R3 M2 M3 (Rk: LDS fragment reads of k-step k,
-    // Mk: its MFMAs), so each k-step's reads are in flight during the previous MFMAs.
+    // Order the slice as R0 R1 M0 R2 M1 ... (Rk: LDS fragment reads of k-step k, Mk: its
+    // MFMAs), so each k-step's reads are in flight during the previous MFMAs.
     __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
 #pragma unroll
-    for (int kk = 1; kk < KSTEPS; ++kk) {
+    for (int kl = 1; kl < KL; ++kl) {
       __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, (KIND == KIND_F32 ? 4 : 1) * FM * FN, 0);
     }
@@ -401,6 +436,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(const GemmParams
 #endif
   }
   wait_vmcnt<0>();
+
+  if constexpr (KS == 2) {
+    // The second k-group hands its partial sums to the first through LDS.
+    float* red = reinterpret_cast<float*>(lds);
+    __syncthreads();
+    if (kgrp == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) red[((i * FN + j) * 16 + e) * (64 * NWC) + wloc * 64 + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (kgrp == 1) return;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] += red[((i * FN + j) * 16 + e) * (64 * NWC) + wloc * 64 + lane];
+  }
 
   epilogue<KIND, BM, BN, WM, WN, SYM, EPI, FM, FN, TO>(p, acc, mat, tm, tn, m0, n0, wm0, wn0, lane);
 }
@@ -568,10 +625,10 @@ hipError_t launch_shape(const GemmParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int NS, bool SYM, int EPI, int TAG>
+template <int KIND, int BM, int BN, int WM, int WN, int NS, bool SYM, int EPI, int TAG, int KS = 1>
 hipError_t launch_dma(const GemmParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_dma_kernel<KIND, BM, BN, WM, WN, NS, SYM, EPI, TAG>), dim3(p.tiles, p.count),
-                     dim3(64 * WM * WN), 0, st, p);
+  hipLaunchKernelGGL((gemm_dma_kernel<KIND, BM, BN, WM, WN, NS, KS, SYM, EPI, TAG>), dim3(p.tiles, p.count),
+                     dim3(64 * WM * WN * KS), 0, st, p);
   return hipGetLastError();
 }
 
@@ -599,6 +656,8 @@ hipError_t launch_tile(int cfg, const GemmParams& p, hipStream_t st) {
     case TILE_256_DMA4:
       if constexpr (KIND != KIND_F32) return launch_dma<KIND, 256, 256, 2, 2, 2, SYM, EPI, TAG>(p, st);
       return hipErrorInvalidValue;
+    case TILE_64_DMA_K2: return launch_dma<KIND, 64, 64, 2, 2, 4, SYM, EPI, TAG, 2>(p, st);
+    case TILE_128_DMA_K2: return launch_dma<KIND, 128, 128, 2, 2, 4, SYM, EPI, TAG, 2>(p, st);
   }
   return hipErrorInvalidValue;
 }

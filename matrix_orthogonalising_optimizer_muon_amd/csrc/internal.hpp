@@ -70,14 +70,16 @@ enum TileCfg : int {
   TILE_256x128_DMA = 6,  // as TILE_256x128, 3 LDS stages
   TILE_256_DMA = 7,      // as TILE_256, 2 LDS stages
   TILE_256_DMA4 = 8,     // 256 x 256, 4 waves, wave tile 128 x 128, 2 LDS stages
-  TILE_COUNT = 9
+  TILE_64_DMA_K2 = 9,    // as TILE_64_DMA with 8 waves: two k-groups split every slice
+  TILE_128_DMA_K2 = 10,  // as TILE_128_DMA with 8 waves: two k-groups split every slice
+  TILE_COUNT = 11
 };
 inline int tile_bm(int cfg) {
-  static const int bm[TILE_COUNT] = {64, 128, 256, 256, 64, 128, 256, 256, 256};
+  static const int bm[TILE_COUNT] = {64, 128, 256, 256, 64, 128, 256, 256, 256, 64, 128};
   return bm[cfg];
 }
 inline int tile_bn(int cfg) {
-  static const int bn[TILE_COUNT] = {64, 128, 128, 256, 64, 128, 128, 256, 256};
+  static const int bn[TILE_COUNT] = {64, 128, 128, 256, 64, 128, 128, 256, 256, 64, 128};
   return bn[cfg];
 }
 

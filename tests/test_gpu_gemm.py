@@ -58,8 +58,8 @@ def check_elems(got, ref, K, u_out):
 
 # tile configurations: 0 = 64x64, 1 = 128x128, 2 = 256x128 (apply only), 3 = 256x256;
 # 4-7: the same tiles with direct global -> LDS loads
-SYM_TILES = [0, 1, 3, 4, 5, 7, 8]
-ALL_TILES = [0, 1, 2, 3, 4, 5, 6, 7, 8]
+SYM_TILES = [0, 1, 3, 4, 5, 7, 8, 9, 10]
+ALL_TILES = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
 
 
 @pytest.mark.parametrize("tile", SYM_TILES)
@@ -77,7 +77,7 @@ def test_syrk_bf16(B, ctx, tile, M, K):
     assert np.array_equal(got, got.T)  # mirrored store: exactly symmetric
 
 
-@pytest.mark.parametrize("tile", [0, 1, 4, 5])
+@pytest.mark.parametrize("tile", [0, 1, 4, 5, 9, 10])
 @pytest.mark.parametrize("M,K", [(128, 256), (320, 192)])
 def test_syrk_f32(B, ctx, tile, M, K):
     rng = np.random.default_rng(M + K + tile)
@@ -148,7 +148,7 @@ def test_apply_fp16(B, ctx, tile, M, N, K):
     assert rel(got, ref) < 1e-3
 
 
-@pytest.mark.parametrize("tile", [0, 1, 4, 5])
+@pytest.mark.parametrize("tile", [0, 1, 4, 5, 9, 10])
 def test_apply_f32(B, ctx, tile):
     M, N, K = 192, 448, 128
     rng = np.random.default_rng(tile + 5)

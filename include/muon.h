@@ -154,7 +154,13 @@ int muon_workspace_size(muon_ctx *ctx, const muon_matrix *mats, int count,
  * measured once and cached): unless the context has MUON_FLAG_MODEL_ONLY, the first
  * step that meets a new (stage, shape, batch) times the candidate tile configurations on
  * its own workspace buffers, synchronising the stream once for it, and caches the
- * fastest for the process; later steps make no host synchronisation. */
+ * fastest for the process; later steps make no host synchronisation.
+ * Concurrency: once every shape group of the list has its tiles measured, independent
+ * groups (matrices of one canonical shape) run on up to four streams: `stream` and
+ * streams the context creates on its device at default priority, forked from `stream`
+ * and joined back into it with events, so the work still completes in `stream`'s order
+ * for the caller (also under stream capture). With MUON_FLAG_PROFILE all launches stay
+ * on `stream`. */
 int muon_step(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hparams *hp,
               void *workspace, size_t workspace_bytes, void *stream);
 

@@ -42,6 +42,11 @@ struct muon_ctx {
   std::vector<ProfRecord> records;
   size_t next_event = 0;
   hipEvent_t tune_ev[2] = {nullptr, nullptr};  // events of the tile measurements
+  // Extra streams on which independent shape groups run beside the caller's stream,
+  // forked from it and joined back into it through events (created on first use).
+  std::vector<hipStream_t> lanes;
+  std::vector<hipEvent_t> lane_join;
+  hipEvent_t lane_fork = nullptr;
 };
 
 namespace muon {
@@ -439,6 +444,47 @@ hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* 
     if ((call) != hipSuccess) return MUON_ERR_HIP; \
   } while (0)
 
+// True when every GEMM stage the group will launch already has a measured tile (or the
+// context does not measure): such a group makes no host synchronisation and may run on
+// a stream of its own next to other groups.
+bool group_tuned(const muon_ctx* ctx, const Group& g, const muon_hparams& hp, bool f32) {
+  if (ctx->flags & MUON_FLAG_MODEL_ONLY) return true;
+  const int rounds = total_rounds(hp);
+  const bool more = (g.mode == MUON_NS_PLAIN) ? rounds > 1 : hp.n_segments > 1;
+  const int cnt = static_cast<int>(g.members.size());
+  std::vector<TuneKey> keys = {
+      std::make_tuple(ctx->device, static_cast<int>(OP_SYRK_IN), f32 ? 1 : 0, g.Mp, g.Mp, cnt),
+      std::make_tuple(ctx->device, static_cast<int>(OP_SYM), f32 ? 1 : 0, g.Mp, g.Mp, cnt),
+      std::make_tuple(ctx->device, static_cast<int>(OP_APPLY), f32 ? 1 : 0, g.Mp, g.Np, cnt)};
+  if (more) keys.push_back(std::make_tuple(ctx->device, static_cast<int>(OP_SYRK), f32 ? 1 : 0, g.Mp, g.Mp, cnt));
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  for (const TuneKey& k : keys)
+    if (g_tuned.find(k) == g_tuned.end()) return false;
+  return true;
+}
+
+constexpr int kMaxLanes = 4;  // streams per step, the caller's included
+
+// Creates the context's extra streams and events (default priority) up to `n` lanes.
+bool ensure_lanes(muon_ctx* ctx, int n) {
+  if (!ctx->lane_fork && hipEventCreateWithFlags(&ctx->lane_fork, hipEventDisableTiming) != hipSuccess) {
+    ctx->lane_fork = nullptr;
+    return false;
+  }
+  while (static_cast<int>(ctx->lanes.size()) < n - 1) {
+    hipStream_t st = nullptr;
+    hipEvent_t ev = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return false;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+      (void)hipStreamDestroy(st);
+      return false;
+    }
+    ctx->lanes.push_back(st);
+    ctx->lane_join.push_back(ev);
+  }
+  return true;
+}
+
 int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
   const muon_hparams& hp = *env.hp;
   const bool f32 = env.f32;
@@ -664,11 +710,41 @@ int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
       MUON_HIP(launch_write_table(c, table + b, env.st));
       tm.done();
     }
-    for (const Group& g : plan.groups) {
-      const int r = run_group(g, env, table + g.table_base);
-      if (r != MUON_OK) return r;
+    // Independent shape groups run on up to kMaxLanes streams (largest work first, each
+    // to the least loaded lane) when none of them still has tiles to measure and the
+    // context does not profile; otherwise all run on the caller's stream in order.
+    int nl = std::min<int>(kMaxLanes, static_cast<int>(plan.groups.size()));
+    if (ctx->flags & MUON_FLAG_PROFILE) nl = 1;
+    for (size_t i = 0; nl > 1 && i < plan.groups.size(); ++i)
+      if (!group_tuned(ctx, plan.groups[i], *hp, env.f32)) nl = 1;
+    if (nl > 1 && !ensure_lanes(ctx, nl)) nl = 1;
+    if (nl == 1) {
+      for (const Group& g : plan.groups) {
+        const int r = run_group(g, env, table + g.table_base);
+        if (r != MUON_OK) return r;
+      }
+      return MUON_OK;
     }
-    return MUON_OK;
+    MUON_HIP(hipEventRecord(ctx->lane_fork, env.st));
+    for (int l = 0; l < nl - 1; ++l) MUON_HIP(hipStreamWaitEvent(ctx->lanes[l], ctx->lane_fork, 0));
+    std::vector<double> load(nl, 0.0);
+    int r = MUON_OK;
+    for (const Group& g : plan.groups) {
+      const int l = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+      load[l] += g.work;
+      StepEnv le = env;
+      if (l > 0) le.st = ctx->lanes[l - 1];
+      r = run_group(g, le, table + g.table_base);
+      if (r != MUON_OK) break;
+    }
+    // The caller's stream waits for every lane, also after a failed launch, so nothing
+    // the step enqueued outlives the caller's view of the stream.
+    for (int l = 0; l < nl - 1; ++l) {
+      if (hipEventRecord(ctx->lane_join[l], ctx->lanes[l]) != hipSuccess ||
+          hipStreamWaitEvent(env.st, ctx->lane_join[l], 0) != hipSuccess)
+        r = MUON_ERR_HIP;
+    }
+    return r;
   } catch (...) {
     return MUON_ERR_HIP;
   }
@@ -809,6 +885,12 @@ int muon_destroy(muon_ctx* ctx) {
     }
     for (hipEvent_t ev : ctx->tune_ev)
       if (ev) (void)hipEventDestroy(ev);
+    for (hipStream_t st : ctx->lanes) {
+      (void)hipStreamSynchronize(st);
+      (void)hipStreamDestroy(st);
+    }
+    for (hipEvent_t ev : ctx->lane_join) (void)hipEventDestroy(ev);
+    if (ctx->lane_fork) (void)hipEventDestroy(ctx->lane_fork);
   }
   delete ctx;
   return MUON_OK;

@@ -42,6 +42,20 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kChunks + (chunk ^ ((row ^ (row >> 3)) & 7));
 }
 
+// The same for LDS rows of CH chunks (CH = 8: 128-byte rows as above; CH = 4: 64-byte
+// rows, two per 128 bytes, where rows 2t and 2t+1 share the XOR term so that 8
+// consecutive rows read at one logical chunk still cover all eight 16-byte positions of a
+// 128-byte span).
+template <int CH>
+__device__ __forceinline__ int swz_bits(int row) {
+  static_assert(CH == 8 || CH == 4, "chunks per row");
+  return CH == 8 ? ((row ^ (row >> 3)) & 7) : ((row >> 1) & 3);
+}
+template <int CH>
+__device__ __forceinline__ int swz_ch(int row, int chunk) {
+  return row * CH + (chunk ^ swz_bits<CH>(row));
+}
+
 __device__ __forceinline__ unsigned short f32_to_f16(float f) {
   _Float16 h = static_cast<_Float16>(f);
   return __builtin_bit_cast(unsigned short, h);
@@ -311,24 +325,27 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Same product as gemm_kernel, with operands moved global -> LDS by the CDNA4 direct
 // loads (16 bytes per lane, lane l writing LDS bytes [16 l, 16 l + 16) of the
-// instruction's 1 KB window = 8 rows x 128 bytes). The XOR swizzle moves to the global
-// side: lane l of a window loads logical chunk (l % 8) ^ f(row). NS LDS stages form a
-// ring; slice k + NS - 1 is issued before slice k is computed, so NS - 1 slices of loads
-// are in flight and no staging registers are needed.
-template <int KIND, int BM, int BN, int WM, int WN, int NS, int KS, bool SYM, int EPI, int TAG>
+// instruction's 1 KB window = 64 / CH rows of CH 16-byte chunks). The XOR swizzle moves
+// to the global side: lane l of a window loads logical chunk (l % CH) ^ f(row). NS LDS
+// stages form a ring; slice k + NS - 1 is issued before slice k is computed, so NS - 1
+// slices of loads are in flight and no staging registers are needed. A slice is CH
+// chunks of K per row: CH = 4 halves the slice, so twice as many stages fit in the same
+// LDS and more load latency is covered.
+template <int KIND, int BM, int BN, int WM, int WN, int NS, int KS, int CH, bool SYM, int EPI, int TAG>
 __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmParams p) {
   using TO = typename OutT<KIND>::T;
   constexpr int NWC = WM * WN;                             // waves per k-group (one tile each)
   constexpr int NW = NWC * KS;                             // waves
   constexpr int ES = (KIND == KIND_F32) ? 4 : 2;
   constexpr int VEC = 16 / ES;
-  constexpr int BK = kChunks * VEC;
+  constexpr int BK = CH * VEC;
   constexpr int TWM = BM / WM, TWN = BN / WN;
   constexpr int FM = TWM / 32, FN = TWN / 32;
-  constexpr int IA = BM / (8 * NW), IB = BN / (8 * NW);   // load instructions per wave
-  static_assert(IA * 8 * NW == BM && IB * 8 * NW == BN, "rows per wave");
-  constexpr int STAGE = (BM + BN) * kChunks;               // u32x4 per stage
-  constexpr int KSTEPS = kChunks / 2;
+  constexpr int RPI = 64 / CH;                             // rows per load instruction
+  constexpr int IA = BM / (RPI * NW), IB = BN / (RPI * NW);  // load instructions per wave
+  static_assert(IA * RPI * NW == BM && IB * RPI * NW == BN, "rows per wave");
+  constexpr int STAGE = (BM + BN) * CH;                    // u32x4 per stage
+  constexpr int KSTEPS = CH / 2;
   constexpr int KL = KSTEPS / KS;                          // k-steps per wave per slice
   constexpr int D = NS - 1;                                // slices in flight
   static_assert(NS >= 2 && (KS == 1 || KS == 2), "stages / k-groups");
@@ -353,15 +370,15 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   int64_t a_off[IA], b_off[IB];
 #pragma unroll
   for (int j = 0; j < IA; ++j) {
-    const int row = (wave * IA + j) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const int row = (wave * IA + j) * RPI + lane / CH;
+    const int chunk = (lane % CH) ^ swz_bits<CH>(row);
     const int gr = min(m0 + row, p.M - 1);
     a_off[j] = (static_cast<int64_t>(gr) * p.lda + chunk * VEC) * ES;
   }
 #pragma unroll
   for (int j = 0; j < IB; ++j) {
-    const int row = (wave * IB + j) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const int row = (wave * IB + j) * RPI + lane / CH;
+    const int chunk = (lane % CH) ^ swz_bits<CH>(row);
     const int gr = min(n0 + row, p.N - 1);
     b_off[j] = (static_cast<int64_t>(gr) * p.ldb + chunk * VEC) * ES;
   }
@@ -371,15 +388,15 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   auto issue = [&](int stage, int k0) {
     const int64_t kb = static_cast<int64_t>(k0) * ES;
     u32x4* sa = lds + stage * STAGE;
-    u32x4* sb = sa + BM * kChunks;
+    u32x4* sb = sa + BM * CH;
 #pragma unroll
     for (int j = 0; j < IA; ++j)
       __builtin_amdgcn_global_load_lds((glb_ptr)(Ab + a_off[j] + kb),
-                                       (lds_ptr)(sa + (wave * IA + j) * 8 * kChunks), 16, 0, 0);
+                                       (lds_ptr)(sa + (wave * IA + j) * RPI * CH), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < IB; ++j)
       __builtin_amdgcn_global_load_lds((glb_ptr)(Bb + b_off[j] + kb),
-                                       (lds_ptr)(sb + (wave * IB + j) * 8 * kChunks), 16, 0, 0);
+                                       (lds_ptr)(sb + (wave * IB + j) * RPI * CH), 16, 0, 0);
   };
 
   f32x16 acc[FM][FN];
@@ -399,9 +416,9 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   auto load_frags = [&](int buf, const u32x4* la, const u32x4* lb, int kk) {
     const int ch = 2 * kk + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[buf][i] = la[swz(wm0 + i * 32 + (lane & 31), ch)];
+    for (int i = 0; i < FM; ++i) fa[buf][i] = la[swz_ch<CH>(wm0 + i * 32 + (lane & 31), ch)];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[buf][j] = lb[swz(wn0 + j * 32 + (lane & 31), ch)];
+    for (int j = 0; j < FN; ++j) fb[buf][j] = lb[swz_ch<CH>(wn0 + j * 32 + (lane & 31), ch)];
   };
 
   // Prologue: slices 0 .. D-1 (clamped: past the end the last slice is reloaded into a
@@ -413,7 +430,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
     __builtin_amdgcn_s_barrier();         // ... and every wave's; slice kt-1's stage is free
     issue((kt + D) % NS, min(kt + D, nk - 1) * BK);
     const u32x4* la = lds + (kt % NS) * STAGE;
-    const u32x4* lb = la + BM * kChunks;
+    const u32x4* lb = la + BM * CH;
     load_frags(0, la, lb, kk0);
 #pragma unroll
     for (int kl = 0; kl < KL; ++kl) {
@@ -625,9 +642,9 @@ hipError_t launch_shape(const GemmParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int NS, bool SYM, int EPI, int TAG, int KS = 1>
+template <int KIND, int BM, int BN, int WM, int WN, int NS, bool SYM, int EPI, int TAG, int KS = 1, int CH = 8>
 hipError_t launch_dma(const GemmParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_dma_kernel<KIND, BM, BN, WM, WN, NS, KS, SYM, EPI, TAG>), dim3(p.tiles, p.count),
+  hipLaunchKernelGGL((gemm_dma_kernel<KIND, BM, BN, WM, WN, NS, KS, CH, SYM, EPI, TAG>), dim3(p.tiles, p.count),
                      dim3(64 * WM * WN * KS), 0, st, p);
   return hipGetLastError();
 }
@@ -658,6 +675,10 @@ hipError_t launch_tile(int cfg, const GemmParams& p, hipStream_t st) {
       return hipErrorInvalidValue;
     case TILE_64_DMA_K2: return launch_dma<KIND, 64, 64, 2, 2, 4, SYM, EPI, TAG, 2>(p, st);
     case TILE_128_DMA_K2: return launch_dma<KIND, 128, 128, 2, 2, 4, SYM, EPI, TAG, 2>(p, st);
+    case TILE_256_DMA_H:  // 64-byte slices: 4 stages, three slices in flight
+      if constexpr (KIND != KIND_F32) return launch_dma<KIND, 256, 256, 2, 4, 4, SYM, EPI, TAG, 1, 4>(p, st);
+      return hipErrorInvalidValue;
+    case TILE_128_DMA_K2_H: return launch_dma<KIND, 128, 128, 2, 2, 8, SYM, EPI, TAG, 2, 4>(p, st);
   }
   return hipErrorInvalidValue;
 }

@@ -57,9 +57,9 @@ enum GemmOp : int {
   OP_SYRK = 4,     // X X^T on the fp16 / fp32 iterate (same kernel as OP_SYM, own symbol)
 };
 
-// Workgroup tile configurations (4 waves each). Symmetric-output stages need BM == BN.
-// Configurations 0-3 stage operands through registers; 4-8 use the CDNA4 direct
-// global -> LDS loads with a multi-stage LDS ring.
+// Workgroup tile configurations. Symmetric-output stages need BM == BN. Configurations
+// 0-3 stage operands through registers; 4-12 use the CDNA4 direct global -> LDS loads
+// with a multi-stage LDS ring.
 enum TileCfg : int {
   TILE_64 = 0,           // 64 x 64, 4 waves, wave tile 32 x 32
   TILE_128 = 1,          // 128 x 128, 4 waves, wave tile 64 x 64
@@ -72,14 +72,16 @@ enum TileCfg : int {
   TILE_256_DMA4 = 8,     // 256 x 256, 4 waves, wave tile 128 x 128, 2 LDS stages
   TILE_64_DMA_K2 = 9,    // as TILE_64_DMA with 8 waves: two k-groups split every slice
   TILE_128_DMA_K2 = 10,  // as TILE_128_DMA with 8 waves: two k-groups split every slice
-  TILE_COUNT = 11
+  TILE_256_DMA_H = 11,   // as TILE_256_DMA with 64-byte slices: 4 LDS stages
+  TILE_128_DMA_K2_H = 12,  // as TILE_128_DMA_K2 with 64-byte slices: 8 LDS stages
+  TILE_COUNT = 13
 };
 inline int tile_bm(int cfg) {
-  static const int bm[TILE_COUNT] = {64, 128, 256, 256, 64, 128, 256, 256, 256, 64, 128};
+  static const int bm[TILE_COUNT] = {64, 128, 256, 256, 64, 128, 256, 256, 256, 64, 128, 256, 128};
   return bm[cfg];
 }
 inline int tile_bn(int cfg) {
-  static const int bn[TILE_COUNT] = {64, 128, 128, 256, 64, 128, 128, 256, 256, 64, 128};
+  static const int bn[TILE_COUNT] = {64, 128, 128, 256, 64, 128, 128, 256, 256, 64, 128, 256, 128};
   return bn[cfg];
 }
 

@@ -166,7 +166,7 @@ def test_debug_gemm_validation(hctx):
     P = ctypes.c_void_p(FAKE)
     # f(ctx, kind, ns_dtype, tile_cfg, M, N, K, A, B, E, C, C2, alpha, beta, gamma, oscale, stream)
     assert f(hctx, 3, 1, 0, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
-    assert f(hctx, 0, 1, 11, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 0, 1, 13, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
     assert f(hctx, 0, 1, 6, 256, 256, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
     assert f(hctx, 0, 1, 0, 64, 64, 100, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
     assert f(hctx, 1, 1, 0, 64, 128, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG

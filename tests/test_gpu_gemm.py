@@ -57,9 +57,11 @@ def check_elems(got, ref, K, u_out):
 
 
 # tile configurations: 0 = 64x64, 1 = 128x128, 2 = 256x128 (apply only), 3 = 256x256;
-# 4-7: the same tiles with direct global -> LDS loads
-SYM_TILES = [0, 1, 3, 4, 5, 7, 8, 9, 10]
-ALL_TILES = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
+# 4-7: the same tiles with direct global -> LDS loads; 8: 256x256 with 4 waves; 9, 10:
+# 64 and 128 tiles with two k-groups; 11, 12: 256 and 128 (two k-groups) with 64-byte slices
+SYM_TILES = [0, 1, 3, 4, 5, 7, 8, 9, 10, 11, 12]
+ALL_TILES = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12]
+F32_TILES = [0, 1, 4, 5, 9, 10, 12]
 
 
 @pytest.mark.parametrize("tile", SYM_TILES)
@@ -77,7 +79,7 @@ def test_syrk_bf16(B, ctx, tile, M, K):
     assert np.array_equal(got, got.T)  # mirrored store: exactly symmetric
 
 
-@pytest.mark.parametrize("tile", [0, 1, 4, 5, 9, 10])
+@pytest.mark.parametrize("tile", F32_TILES)
 @pytest.mark.parametrize("M,K", [(128, 256), (320, 192)])
 def test_syrk_f32(B, ctx, tile, M, K):
     rng = np.random.default_rng(M + K + tile)
@@ -94,7 +96,7 @@ def test_syrk_f32(B, ctx, tile, M, K):
 @pytest.mark.parametrize("tile", SYM_TILES)
 @pytest.mark.parametrize("ns,dt,u", [("bf16", torch.float16, 2.0 ** -11), ("f32", torch.float32, 2.0 ** -24)])
 def test_square_poly(B, ctx, tile, ns, dt, u):
-    if ns == "f32" and tile in (3, 7, 8):
+    if ns == "f32" and tile not in F32_TILES:
         pytest.skip("256x256 tiles are not built for fp32")
     M = 576
     rng = np.random.default_rng(tile)
@@ -148,7 +150,7 @@ def test_apply_fp16(B, ctx, tile, M, N, K):
     assert rel(got, ref) < 1e-3
 
 
-@pytest.mark.parametrize("tile", [0, 1, 4, 5, 9, 10])
+@pytest.mark.parametrize("tile", F32_TILES)
 def test_apply_f32(B, ctx, tile):
     M, N, K = 192, 448, 128
     rng = np.random.default_rng(tile + 5)

@@ -160,6 +160,33 @@ def test_fp32_split_k(B, ctx):
     check_step(B, ctx, w, mode="plain")
 
 
+def test_concurrent_groups(B, ctx):
+    """Six shape groups: after the first step has measured their tiles, later steps run the
+    groups on several streams. Results match the oracle over three steps, and are bitwise
+    identical to a profiling context, which keeps every launch on one stream."""
+    shapes = [(256, 1024), (128, 512), (512, 128), (64, 256), (192, 192), (96, 320), (448, 64)]
+    w = wl.custom("lanes", shapes, structure="lowrank", rank=8, wid=212, steps=3)
+    hp = B.make_hparams(mode="auto")
+    warm = GpuState(w)
+    warm.load_gradients(0)
+    run_step(ctx, warm, hp)            # measures the tiles of every group
+    mode_of = lambda s: "gram" if max(s.rows, s.cols) / min(s.rows, s.cols) > 1.5 else "plain"
+    check_step(B, ctx, w, mode="gram", gpu_mode="auto", steps=3, mode_of=mode_of)
+    prof = B.muon_init(0, B.MUON_FLAG_PROFILE)
+    try:
+        outs = []
+        for c in (ctx, prof):
+            st = GpuState(w)
+            for s in range(3):
+                st.load_gradients(s)
+                run_step(c, st, hp)
+            outs.append([x.clone() for x in st.W + st.M])
+        for a, b in zip(*outs):
+            assert torch.equal(a, b)
+    finally:
+        B.muon_destroy(prof)
+
+
 def test_small_batch_832_full(B, ctx):
     w = wl.WORKLOADS["small_batch_832"]
     check_step(B, ctx, w, mode="gram", gpu_mode="auto")

@@ -27,7 +27,7 @@ if ROOT not in sys.path:
 
 PEAK = {"bf16": 2500.0, "f32": 157.3}       # dense MFMA TFLOP/s (MI355X public figures)
 HBM_PEAK_GBS = 8000.0
-GEMM_STAGES = ("syrk", "square", "apply", "apply_update")
+GEMM_STAGES = ("syrk_u", "syrk", "square", "apply", "apply_update")
 
 
 def parse():
@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--details", action="store_true", help="also print the per-stage table to stderr")
+    ap.add_argument("--tune-cache", default=None,
+                    help="tile-choice file: loaded before the warmup when it exists, written after "
+                         "it (so that separate profiling runs use the same kernels)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before warmup, copy this many MiB device-to-device once (a plain copy "
                          "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -102,6 +105,36 @@ def cpu_baseline(w, budget_s):
             "sample": sample}
 
 
+TRAFFIC_SOURCES = ("matrix_orthogonalising_optimizer_muon_amd/csrc/gemm.hip",
+                   "matrix_orthogonalising_optimizer_muon_amd/csrc/elementwise.hip",
+                   "matrix_orthogonalising_optimizer_muon_amd/csrc/internal.hpp")
+
+
+def traffic_record(workload):
+    """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE and WRITE_SIZE passes, scaled by
+    a copy of known size), per stage and tile configuration, as recorded in
+    profiles/muon_step_<workload>.md; None when there is no record or the kernel sources
+    changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"muon_step_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("<!-- traffic-record "):
+                rec = json.loads(line[len("<!-- traffic-record "):].rsplit("-->", 1)[0])
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for src in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -143,9 +176,14 @@ def main():
               flush=True)
         del src, dst
 
+    if args.tune_cache and os.path.exists(args.tune_cache):
+        n = B.muon_tune_load(ctx, args.tune_cache)
+        print(f"[bench] {n} tile choices loaded from {args.tune_cache}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step(ctx)
     torch.cuda.synchronize()
+    if args.tune_cache:
+        B.muon_tune_save(ctx, args.tune_cache)
     print(f"[bench] warmup done ({args.warmup} steps), workspace {nbytes / 2**30:.2f} GiB",
           file=sys.stderr, flush=True)
 
@@ -208,7 +246,7 @@ def main():
                    "storage": {"W": w.w_dtype, "G": w.g_dtype, "M": w.m_dtype}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": f"{dom['stage']} m'={dom['m']} n'={dom['n']} x{dom['count']}",
+                     "kernel": f"{dom['stage']} m'={dom['m']} n'={dom['n']} x{dom['count']} tile {dom['tile']}",
                      "avg_launch_us": round(avg_ms * 1e3, 2),
                      "flops_per_launch": per_launch_flops},
         "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
@@ -229,6 +267,14 @@ def main():
         plans[key] = {"mode": {1: "plain", 2: "gram"}[e.mode], "tile_sym": e.tile_sym,
                       "tile_apply": e.tile_apply}
     out["config"]["plan"] = plans
+    rec = traffic_record(w.name)
+    st = rec["kernels"].get(f"{dom['stage']}/{dom['tile']}") if rec else None
+    if st is not None:
+        out["roofline"]["traffic"] = st["fetch_bytes"] + st["write_bytes"]
+        out["roofline"]["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
+        out["roofline"]["traffic_kernel"] = st["kernel"]
+        if "trace_avg_us" in st:
+            out["roofline"]["rocprof_avg_us"] = st["trace_avg_us"]
     B.muon_destroy(ctx)
     B.muon_destroy(pctx)
     print(json.dumps(out), flush=True)

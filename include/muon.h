@@ -111,13 +111,16 @@ typedef struct muon_plan_entry {
   double kernel_flops;   /* FLOPs the kernels actually perform (symmetric outputs halved) */
 } muon_plan_entry;
 
-/* Aggregated launch timings of one stage kind and shape (muon_profile_read). */
+/* Aggregated launch timings of one stage kind, shape and tile (muon_profile_read). */
 typedef struct muon_profile_entry {
-  char stage[32];        /* "table", "momentum", "norm_finalize", "transpose", "syrk",
-                            "square", "apply", "apply_update" */
+  char stage[32];        /* "table", "momentum", "norm_finalize", "transpose", "syrk_u"
+                            (Gram product of the momentum output), "syrk" (of the
+                            iterate), "square", "apply", "apply_update" */
   int64_t m, n;          /* canonical shape of the group the launches served */
   int32_t count;         /* matrices per launch */
   int32_t launches;      /* launches aggregated */
+  int32_t tile;          /* tile configuration of GEMM stages (muon_debug_gemm ids), else -1 */
+  int32_t reserved;
   double total_ms;       /* sum of event-measured launch durations */
   double flops;          /* algorithmic FLOPs of those launches (one triangle for
                             symmetric outputs) */
@@ -164,6 +167,20 @@ int muon_workspace_size(muon_ctx *ctx, const muon_matrix *mats, int count,
 int muon_step(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hparams *hp,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Measured tile choices, shared by every context of the process, to and from a text file,
+ * so that another process starts with the same choices instead of measuring again
+ * (DMuon summary, section 2.4: per-shape configurations measured once and cached). One
+ * choice per line: "stage path padded_m padded_n batch tile" (stage: 0 Gram product of
+ * the momentum output, 1 m' x m' product, 2 apply, 4 Gram product of the iterate; path:
+ * 0 bf16, 1 fp32; tile: as in muon_debug_gemm). muon_tune_save writes the choices made on
+ * the context's device (overwriting the file). muon_tune_load validates the whole file
+ * first and then adds its choices for the context's device, replacing choices already
+ * held for the same key; *n_loaded (may be null) receives their number. A missing or
+ * unreadable file, a malformed line or a tile unavailable for its stage returns
+ * MUON_ERR_ARG and changes nothing. Host-only contexts save and load too. */
+int muon_tune_save(muon_ctx *ctx, const char *path);
+int muon_tune_load(muon_ctx *ctx, const char *path, int *n_loaded);
+
 /* Plan of matrix `index` of the list (host-only; nothing is launched). */
 int muon_plan_info(muon_ctx *ctx, const muon_matrix *mats, int count,
                    const muon_hparams *hp, int index, muon_plan_entry *out);
@@ -177,8 +194,13 @@ int muon_plan_info(muon_ctx *ctx, const muon_matrix *mats, int count,
  *   kind 2: v = alpha * A B^T + beta * E^T with E stored N x M (may be null);
  *           C (M x N) = oscale * v and, if C2 is not null, C2 (N x M) = oscale * v^T;
  *           operands and outputs fp16 (MUON_BF16) or fp32.
- * tile selects the workgroup tile: 0 = 64x64, 1 = 128x128, 2 = 256x128 (kind 2 only),
- * 3 = 256x256 (not fp32); an unavailable combination returns MUON_ERR_UNSUPPORTED.
+ * tile selects the workgroup tile configuration (operands staged through registers:
+ * 0 = 64x64, 1 = 128x128, 2 = 256x128 (kind 2 only), 3 = 256x256; with direct global->LDS
+ * loads: 4 = 64x64, 5 = 128x128, 6 = 256x128 (kind 2 only), 7 = 256x256, 8 = 256x256 with
+ * 4 waves, 9 = 64x64 and 10 = 128x128 with two k-groups, 11 = 256x256 with 64-byte K
+ * slices, 12 = 128x128 with two k-groups and 64-byte K slices; 2, 3, 6, 7, 8 and 11 not
+ * fp32);
+ * an unavailable combination returns MUON_ERR_UNSUPPORTED.
  * Leading dimensions equal the column counts; M, N, K must be multiples of 64. */
 int muon_debug_gemm(muon_ctx *ctx, int kind, int ns_dtype, int tile, int64_t M, int64_t N,
                     int64_t K, const void *A, const void *B, const void *E, void *C, void *C2,
@@ -186,7 +208,7 @@ int muon_debug_gemm(muon_ctx *ctx, int kind, int ns_dtype, int tile, int64_t M, 
 
 /* Profiler read-out for a context created with MUON_FLAG_PROFILE: waits for the last
  * recorded launch, aggregates all launches recorded since the previous read by (stage,
- * shape, batch) in first-seen order into out[0..capacity), stores the number of entries
+ * shape, batch, tile) in first-seen order into out[0..capacity), stores the number of entries
  * in *n_out and clears the record. Returns MUON_ERR_ARG when the context was created
  * without the flag or when more than `capacity` entries exist (then *n_out tells how
  * many are needed and the record is cleared). */

@@ -72,6 +72,7 @@ class muon_plan_entry(ctypes.Structure):
 class muon_profile_entry(ctypes.Structure):
     _fields_ = [("stage", ctypes.c_char * 32), ("m", ctypes.c_int64), ("n", ctypes.c_int64),
                 ("count", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
                 ("bytes", ctypes.c_double)]
 
@@ -98,6 +99,10 @@ _lib.muon_debug_gemm.restype = ctypes.c_int
 _lib.muon_profile_read.argtypes = [_P, ctypes.POINTER(muon_profile_entry), ctypes.c_int,
                                    ctypes.POINTER(ctypes.c_int)]
 _lib.muon_profile_read.restype = ctypes.c_int
+_lib.muon_tune_save.argtypes = [_P, ctypes.c_char_p]
+_lib.muon_tune_save.restype = ctypes.c_int
+_lib.muon_tune_load.argtypes = [_P, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int)]
+_lib.muon_tune_load.restype = ctypes.c_int
 _lib.muon_destroy.argtypes = [_P]
 _lib.muon_destroy.restype = ctypes.c_int
 _lib.muon_status_str.argtypes = [ctypes.c_int]
@@ -218,7 +223,17 @@ def muon_profile_read(ctx, capacity: int = 256) -> list:
     n = ctypes.c_int()
     check(_lib.muon_profile_read(ctx, buf, capacity, ctypes.byref(n)), "muon_profile_read")
     return [dict(stage=e.stage.decode(), m=e.m, n=e.n, count=e.count, launches=e.launches,
-                 total_ms=e.total_ms, flops=e.flops, bytes=e.bytes) for e in buf[:n.value]]
+                 tile=e.tile, total_ms=e.total_ms, flops=e.flops, bytes=e.bytes) for e in buf[:n.value]]
+
+
+def muon_tune_save(ctx, path: str) -> None:
+    check(_lib.muon_tune_save(ctx, os.fsencode(path)), "muon_tune_save")
+
+
+def muon_tune_load(ctx, path: str) -> int:
+    n = ctypes.c_int()
+    check(_lib.muon_tune_load(ctx, os.fsencode(path), ctypes.byref(n)), "muon_tune_load")
+    return n.value
 
 
 def muon_destroy(ctx) -> int:
@@ -228,6 +243,6 @@ def muon_destroy(ctx) -> int:
 def exported_symbols() -> list:
     """Names of the C entry points this binding resolved (each must exist in the .so)."""
     return [n for n in ("muon_hparams_default", "muon_init", "muon_workspace_size", "muon_step",
-                        "muon_plan_info", "muon_debug_gemm", "muon_profile_read", "muon_destroy",
-                        "muon_status_str")
+                        "muon_plan_info", "muon_debug_gemm", "muon_profile_read", "muon_tune_save",
+                        "muon_tune_load", "muon_destroy", "muon_status_str")
             if hasattr(_lib, n)]

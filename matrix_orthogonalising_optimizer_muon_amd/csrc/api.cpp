@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -32,6 +33,7 @@ struct ProfRecord {
   int64_t m, n;        // canonical shape of the group
   int count;           // matrices in the launch
   double flops, bytes; // algorithmic work of the launch
+  int tile;            // GEMM tile configuration, -1 for other stages
 };
 
 struct muon_ctx {
@@ -243,9 +245,12 @@ struct StepEnv {
   muon_ctx* ctx;
 };
 
+// One stage name per kernel symbol: "syrk_u" is the Gram product of the momentum output
+// (bf16 operands on the bf16 path), "syrk" the one of the fp16 / fp32 iterate.
 constexpr const char* kStageNames[] = {"table", "momentum", "norm_finalize", "transpose", "syrk",
-                                       "square", "apply", "apply_update"};
-enum Stage { ST_TABLE, ST_MOMENTUM, ST_FINALIZE, ST_TRANSPOSE, ST_SYRK, ST_SQUARE, ST_APPLY, ST_UPDATE };
+                                       "square", "apply", "apply_update", "syrk_u"};
+enum Stage { ST_TABLE, ST_MOMENTUM, ST_FINALIZE, ST_TRANSPOSE, ST_SYRK, ST_SQUARE, ST_APPLY, ST_UPDATE,
+             ST_SYRK_U };
 constexpr size_t kMaxRecords = 1 << 16;
 
 // Brackets one launch with events when profiling is on (no effect otherwise).
@@ -266,7 +271,7 @@ struct StageTimer {
     const auto ev = c->event_pool[c->next_event];
     if (hipEventRecord(ev.first, s) != hipSuccess) return;
     ctx = c; st = s; on = true;
-    rec = ProfRecord{ev.first, ev.second, stage, m, n, count, flops, bytes};
+    rec = ProfRecord{ev.first, ev.second, stage, m, n, count, flops, bytes, -1};
   }
   void done() {
     if (!on) return;
@@ -315,7 +320,7 @@ std::map<TuneKey, int> g_tuned;
 
 template <class Build>
 hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristic, bool sym,
-                     Build build) {
+                     Build build, int* used) {
   muon_ctx* ctx = env.ctx;
   int cfg = heuristic;
   if (!(ctx->flags & MUON_FLAG_MODEL_ONLY)) {
@@ -329,6 +334,9 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
       if (it != g_tuned.end()) { cfg = it->second; found = true; }
     }
     if (!found) {
+      // Each candidate: one warm-up and two timed launches, its time the faster of the two.
+      // The first candidate (in the order below) within 2% of the fastest wins, so that
+      // near-ties resolve the same way from run to run.
       std::vector<int> cands;
       if (env.f32) {
         cands = {TILE_64, TILE_128, TILE_64_DMA, TILE_128_DMA, TILE_128_DMA_K2};
@@ -345,23 +353,30 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
       for (int i = 0; i < 2; ++i)
         if (!ctx->tune_ev[i] && hipEventCreate(&ctx->tune_ev[i]) != hipSuccess) return hipErrorUnknown;
       const GemmOp top = (op == OP_UPDATE) ? OP_APPLY : op;
-      float best = 1e30f;
-      for (int c : cands) {
+      std::vector<float> times(cands.size(), 1e30f);
+      for (size_t ci = 0; ci < cands.size(); ++ci) {
+        const int c = cands[ci];
         const GemmParams p = build(c);
         if (launch_gemm(top, env.f32, c, p, env.st) != hipSuccess) continue;  // warm-up
-        if (hipEventRecord(ctx->tune_ev[0], env.st) != hipSuccess) return hipErrorUnknown;
-        if (launch_gemm(top, env.f32, c, p, env.st) != hipSuccess) return hipErrorUnknown;
-        if (hipEventRecord(ctx->tune_ev[1], env.st) != hipSuccess) return hipErrorUnknown;
-        if (hipEventSynchronize(ctx->tune_ev[1]) != hipSuccess) return hipErrorUnknown;
-        float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, ctx->tune_ev[0], ctx->tune_ev[1]) != hipSuccess) return hipErrorUnknown;
-        if (ms < best) { best = ms; cfg = c; }
+        for (int rep = 0; rep < 2; ++rep) {
+          if (hipEventRecord(ctx->tune_ev[0], env.st) != hipSuccess) return hipErrorUnknown;
+          if (launch_gemm(top, env.f32, c, p, env.st) != hipSuccess) return hipErrorUnknown;
+          if (hipEventRecord(ctx->tune_ev[1], env.st) != hipSuccess) return hipErrorUnknown;
+          if (hipEventSynchronize(ctx->tune_ev[1]) != hipSuccess) return hipErrorUnknown;
+          float ms = 0.0f;
+          if (hipEventElapsedTime(&ms, ctx->tune_ev[0], ctx->tune_ev[1]) != hipSuccess) return hipErrorUnknown;
+          times[ci] = std::min(times[ci], ms);
+        }
       }
+      const float best = *std::min_element(times.begin(), times.end());
+      for (size_t ci = 0; ci < cands.size(); ++ci)
+        if (times[ci] <= best * 1.02f) { cfg = cands[ci]; break; }
       std::lock_guard<std::mutex> lk(g_tune_mu);
       g_tuned[key] = cfg;
     }
   }
   const GemmParams p = build(cfg);
+  *used = cfg;
   return launch_gemm(op, env.f32, cfg, p, env.st);
 }
 
@@ -380,8 +395,8 @@ hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, floa
     return p;
   };
   const double cnt = static_cast<double>(g.members.size());
-  StageTimer tm(env.ctx, env.st, ST_SYRK, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.n, 0.0);
-  const hipError_t e = run_stage(env, g, input ? OP_SYRK_IN : OP_SYRK, g.tile_sq, true, build);
+  StageTimer tm(env.ctx, env.st, input ? ST_SYRK_U : ST_SYRK, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.n, 0.0);
+  const hipError_t e = run_stage(env, g, input ? OP_SYRK_IN : OP_SYRK, g.tile_sq, true, build, &tm.rec.tile);
   tm.done();
   return e;
 }
@@ -401,7 +416,7 @@ hipError_t square(const Group& g, const StepEnv& env, const void* A, const void*
   };
   const double cnt = static_cast<double>(g.members.size());
   StageTimer tm(env.ctx, env.st, ST_SQUARE, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.m, 0.0);
-  const hipError_t e = run_stage(env, g, OP_SYM, g.tile_sq, true, build);
+  const hipError_t e = run_stage(env, g, OP_SYM, g.tile_sq, true, build, &tm.rec.tile);
   tm.done();
   return e;
 }
@@ -434,7 +449,7 @@ hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* 
   const double wbytes = update ? cnt * g.m * g.n * 2.0 * (env.hp->w_dtype == MUON_BF16 ? 2.0 : 4.0) : 0.0;
   StageTimer tm(env.ctx, env.st, update ? ST_UPDATE : ST_APPLY, g.m, g.n, static_cast<int>(cnt),
                 cnt * 2.0 * g.m * g.m * g.n, wbytes);
-  const hipError_t e = run_stage(env, g, update ? OP_UPDATE : OP_APPLY, g.tile_ap, false, build);
+  const hipError_t e = run_stage(env, g, update ? OP_UPDATE : OP_APPLY, g.tile_ap, false, build, &tm.rec.tile);
   tm.done();
   return e;
 }
@@ -750,6 +765,72 @@ int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
   }
 }
 
+int muon_tune_save(muon_ctx* ctx, const char* path) {
+  try {
+    if (!ctx || !path) return MUON_ERR_ARG;
+    std::vector<std::pair<TuneKey, int>> rows;
+    {
+      std::lock_guard<std::mutex> lk(g_tune_mu);
+      for (const auto& kv : g_tuned)
+        if (std::get<0>(kv.first) == ctx->device) rows.push_back(kv);
+    }
+    FILE* f = std::fopen(path, "w");
+    if (!f) return MUON_ERR_ARG;
+    bool ok = true;
+    for (const auto& kv : rows) {
+      const TuneKey& k = kv.first;
+      ok = ok && std::fprintf(f, "%d %d %lld %lld %d %d\n", std::get<1>(k), std::get<2>(k),
+                              static_cast<long long>(std::get<3>(k)), static_cast<long long>(std::get<4>(k)),
+                              std::get<5>(k), kv.second) > 0;
+    }
+    ok = (std::fclose(f) == 0) && ok;
+    return ok ? MUON_OK : MUON_ERR_ARG;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+int muon_tune_load(muon_ctx* ctx, const char* path, int* n_loaded) {
+  try {
+    if (n_loaded) *n_loaded = 0;
+    if (!ctx || !path) return MUON_ERR_ARG;
+    FILE* f = std::fopen(path, "r");
+    if (!f) return MUON_ERR_ARG;
+    std::vector<std::pair<TuneKey, int>> rows;
+    bool ok = true;
+    char line[256];
+    while (ok && std::fgets(line, sizeof(line), f)) {
+      int op = 0, f32 = 0, cnt = 0, tile = 0, used = 0;
+      long long mp = 0, np = 0;
+      bool blank = true;
+      for (const char* c = line; *c; ++c)
+        if (*c != ' ' && *c != '\t' && *c != '\n' && *c != '\r') blank = false;
+      if (blank) continue;
+      if (std::sscanf(line, "%d %d %lld %lld %d %d %n", &op, &f32, &mp, &np, &cnt, &tile, &used) != 6 ||
+          line[used] != '\0') {
+        ok = false;
+        break;
+      }
+      const bool sym = op == OP_SYRK_IN || op == OP_SYM || op == OP_SYRK;
+      ok = (sym || op == OP_APPLY) && (f32 == 0 || f32 == 1) && mp >= kPad && np >= kPad &&
+           mp % kPad == 0 && np % kPad == 0 && mp <= kMaxDim && np <= kMaxDim && cnt >= 1 &&
+           cnt <= kMaxBatch && tile >= 0 && tile < TILE_COUNT && (!sym || mp == np) &&
+           tile_available(sym, f32 == 1, tile);
+      if (ok) rows.emplace_back(std::make_tuple(ctx->device, op, f32, static_cast<int64_t>(mp),
+                                                static_cast<int64_t>(np), cnt), tile);
+    }
+    ok = ok && !std::ferror(f);
+    std::fclose(f);
+    if (!ok) return MUON_ERR_ARG;
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    for (const auto& kv : rows) g_tuned[kv.first] = kv.second;
+    if (n_loaded) *n_loaded = static_cast<int>(rows.size());
+    return MUON_OK;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
 int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams* hp,
                    int index, muon_plan_entry* out) {
   try {
@@ -841,18 +922,18 @@ int muon_profile_read(muon_ctx* ctx, muon_profile_entry* out, int capacity, int*
     DeviceGuard dg(ctx->device);
     if (!dg.ok) return MUON_ERR_HIP;
     if (hipEventSynchronize(ctx->records.back().stop) != hipSuccess) return MUON_ERR_HIP;
-    std::map<std::tuple<int, int64_t, int64_t, int>, muon_profile_entry> agg;
-    std::vector<std::tuple<int, int64_t, int64_t, int>> order;
+    std::map<std::tuple<int, int64_t, int64_t, int, int>, muon_profile_entry> agg;
+    std::vector<std::tuple<int, int64_t, int64_t, int, int>> order;
     for (const ProfRecord& r : ctx->records) {
       float ms = 0.0f;
       if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return MUON_ERR_HIP;
-      const auto key = std::make_tuple(r.stage, r.m, r.n, r.count);
+      const auto key = std::make_tuple(r.stage, r.m, r.n, r.count, r.tile);
       auto it = agg.find(key);
       if (it == agg.end()) {
         muon_profile_entry e;
         std::memset(&e, 0, sizeof(e));
         std::strncpy(e.stage, kStageNames[r.stage], sizeof(e.stage) - 1);
-        e.m = r.m; e.n = r.n; e.count = r.count;
+        e.m = r.m; e.n = r.n; e.count = r.count; e.tile = r.tile;
         it = agg.emplace(key, e).first;
         order.push_back(key);
       }

@@ -85,6 +85,15 @@ inline int tile_bn(int cfg) {
   return bn[cfg];
 }
 
+// Whether launch_gemm has configuration `cfg` for a symmetric-output (sym) or general
+// stage on the fp32 (f32) or bf16 path.
+inline bool tile_available(bool sym, bool f32, int cfg) {
+  if (cfg < 0 || cfg >= TILE_COUNT) return false;
+  if (sym && tile_bm(cfg) != tile_bn(cfg)) return false;
+  if (f32 && tile_bm(cfg) == 256) return false;
+  return true;
+}
+
 // Launch one batched GEMM stage. ns_f32: fp32 kernels, else bf16/fp16 kernels.
 hipError_t launch_gemm(GemmOp op, bool ns_f32, int cfg, const GemmParams& p, hipStream_t st);
 

@@ -227,3 +227,44 @@ def test_workspace_size_is_deterministic_and_grows(hctx):
     assert two > one
     f32 = B.muon_workspace_size(hctx, [(0, 0, 0, 256, 1024)], B.make_hparams(ns_dtype="f32"))
     assert f32 > one
+
+
+# ---------------------------------------------------------------- tile cache file
+
+def test_tune_cache_round_trip(hctx, tmp_path):
+    """Choices loaded from a file are the ones plan_info reports and are written back
+    unchanged (a host-only context keeps its own device key, so GPU runs are unaffected)."""
+    src = tmp_path / "tune.txt"
+    src.write_text("1 0 2560 2560 1 10\n2 0 2560 9728 1 7\n\n0 0 2560 2560 1 5\n4 0 2560 2560 1 12\n")
+    assert B.muon_tune_load(hctx, str(src)) == 4
+    e = B.muon_plan_info(hctx, [(0, 0, 0, 2560, 9728)], B.make_hparams(), 0)
+    assert (e.tile_sym, e.tile_apply) == (10, 7)
+    out = tmp_path / "out.txt"
+    B.muon_tune_save(hctx, str(out))
+    got = sorted(tuple(map(int, l.split())) for l in out.read_text().splitlines())
+    assert got == sorted([(0, 0, 2560, 2560, 1, 5), (1, 0, 2560, 2560, 1, 10), (2, 0, 2560, 9728, 1, 7),
+                          (4, 0, 2560, 2560, 1, 12)])
+
+
+@pytest.mark.parametrize("text", [
+    "1 0 2560 2560 1\n",            # missing field
+    "1 0 2560 2560 1 10 3\n",       # extra field
+    "3 0 2560 9728 1 7\n",          # the update stage shares the apply's choice
+    "1 0 2560 9728 1 10\n",         # symmetric stage with m != n
+    "1 0 2560 2560 1 6\n",          # 256x128 tile for a symmetric stage
+    "2 1 2560 9728 1 7\n",          # 256 tile on the fp32 path
+    "2 0 2500 9728 1 1\n",          # not a multiple of 64
+    "2 0 2560 9728 0 1\n",          # empty batch
+    "2 0 2560 9728 1 13\n",         # unknown tile
+    "2 0 2560 9728 1 x\n",
+])
+def test_tune_cache_rejects_bad_files(hctx, tmp_path, text):
+    f = tmp_path / "bad.txt"
+    f.write_text("2 0 640 1280 3 1\n" + text)
+    before = B.muon_plan_info(hctx, [(0, 0, 0, 640, 1280)] * 3, B.make_hparams(), 0).tile_apply
+    with pytest.raises(B.MuonError):
+        B.muon_tune_load(hctx, str(f))
+    # nothing of the file was taken, also not its valid first line
+    assert B.muon_plan_info(hctx, [(0, 0, 0, 640, 1280)] * 3, B.make_hparams(), 0).tile_apply == before
+    with pytest.raises(B.MuonError):
+        B.muon_tune_load(hctx, str(tmp_path / "missing.txt"))

@@ -58,9 +58,7 @@ def make_inputs(w, torch):
             Ws.append(torch.from_numpy(wl.weight_np(w, i)).to("cuda").to(tdt[w.w_dtype]))
             Gs.append(torch.from_numpy(wl.gradient_np(w, 0, i)).to("cuda").to(tdt[w.g_dtype]))
         else:
-            gen = torch.Generator(device="cuda")
-            gen.manual_seed(1000 + i)
-            Ws.append((0.02 * torch.randn(spec.rows, spec.cols, generator=gen, device="cuda")).to(tdt[w.w_dtype]))
+            Ws.append(wl.weight_torch(w, i, "cuda"))
             Gs.append(wl.gradient_torch(w, 0, i, "cuda"))
         Ms.append(torch.zeros(spec.rows, spec.cols, dtype=tdt[w.m_dtype], device="cuda"))
     return Ws, Gs, Ms, ("seeded numpy draw" if host else "seeded torch device draw")

@@ -185,3 +185,15 @@ def gradient_torch(w: Workload, step: int, index: int, device="cuda", spec: Matr
         G = (Ub * s) @ Vb.T
         G += w.noise * torch.randn(rows, cols, generator=gen, device=device)
     return G.to(torch.bfloat16 if w.g_dtype == "bf16" else torch.float32)
+
+
+def weight_torch(w: Workload, index: int, device="cuda", spec: MatrixSpec | None = None):
+    """Device-side initial weight, 0.02 * N(0, 1) from torch's generator (seeded per matrix),
+    in the weight's storage dtype."""
+    import torch
+
+    spec = spec or w.matrices[index]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(np.random.SeedSequence([w.wid, 0, index, 8]).generate_state(1)[0]))
+    W = 0.02 * torch.randn(spec.rows, spec.cols, generator=gen, device=device)
+    return W.to(torch.bfloat16 if w.w_dtype == "bf16" else torch.float32)

@@ -54,6 +54,7 @@ extern "C" {
 /* ---- muon_init flags ---- */
 #define MUON_FLAG_MODEL_ONLY 1u  /* no timed tile tuning: static tile choice only */
 #define MUON_FLAG_PROFILE 2u     /* bracket every launch with hipEvents (muon_profile_read) */
+#define MUON_FLAG_STAGED_ONLY 4u /* never use the single-workgroup kernel for small matrices */
 
 typedef struct muon_ctx muon_ctx; /* opaque; owned by the library */
 
@@ -106,9 +107,14 @@ typedef struct muon_plan_entry {
   int32_t tile_sym;      /* tile configuration of the m' x m' products (muon_debug_gemm ids):
                             the measured choice once a step has run, else the static one */
   int32_t tile_apply;    /* tile configuration of the apply products, likewise */
-  int32_t reserved;
+  int32_t single_wg;     /* 1: the whole update of each matrix runs in one workgroup of
+                            one launch; chosen on the bf16 path when every matrix of the list
+                            has m' <= 128 and m' n' <= 65536 after padding to multiples of
+                            64 (without MUON_FLAG_STAGED_ONLY); tile_sym and tile_apply are
+                            then -1 */
   double dense_flops;    /* matmul FLOPs as the MuonX article counts them (2m'^2n', 2m'^3) */
-  double kernel_flops;   /* FLOPs the kernels actually perform (symmetric outputs halved) */
+  double kernel_flops;   /* FLOPs the kernels actually perform (symmetric outputs halved on
+                            the staged path; dense in the single-workgroup kernel) */
 } muon_plan_entry;
 
 /* Aggregated launch timings of one stage kind, shape and tile (muon_profile_read). */
@@ -135,7 +141,8 @@ void muon_hparams_default(muon_hparams *hp);
  * MUON_ERR_DEVICE. device == -1 creates a host-only context (no HIP call is made; it
  * plans for a 256-CU MI355X): muon_workspace_size and muon_plan_info work, muon_step and
  * muon_debug_gemm validate their arguments and then return MUON_ERR_DEVICE.
- * `flags` is 0 or a combination of MUON_FLAG_MODEL_ONLY and MUON_FLAG_PROFILE. *out receives the context; it is owned by the
+ * `flags` is 0 or a combination of MUON_FLAG_MODEL_ONLY, MUON_FLAG_PROFILE and
+ * MUON_FLAG_STAGED_ONLY. *out receives the context; it is owned by the
  * caller until muon_destroy. No device memory is allocated. */
 int muon_init(muon_ctx **out, int device, uint32_t flags);
 

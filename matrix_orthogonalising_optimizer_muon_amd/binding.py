@@ -41,6 +41,7 @@ MUON_NS_GRAM = 2
 MUON_MAX_SEGMENTS = 8
 MUON_FLAG_MODEL_ONLY = 1
 MUON_FLAG_PROFILE = 2
+MUON_FLAG_STAGED_ONLY = 4
 
 DTYPES = {"f32": MUON_F32, "bf16": MUON_BF16}
 MODES = {"auto": MUON_NS_AUTO, "plain": MUON_NS_PLAIN, "gram": MUON_NS_GRAM}
@@ -65,7 +66,7 @@ class muon_plan_entry(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("transposed", ctypes.c_int32),
                 ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("group", ctypes.c_int32),
                 ("tile_sym", ctypes.c_int32), ("tile_apply", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("dense_flops", ctypes.c_double),
+                ("single_wg", ctypes.c_int32), ("dense_flops", ctypes.c_double),
                 ("kernel_flops", ctypes.c_double)]
 
 

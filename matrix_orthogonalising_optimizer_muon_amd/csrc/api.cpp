@@ -77,6 +77,7 @@ struct Group {
   size_t off_partials = 0, off_s = 0, off_x = 0, off_xt[2] = {0, 0}, off_sq[4] = {0, 0, 0, 0};
   int64_t stride_x = 0, stride_sq = 0;
   int mom_tiles_m = 0, mom_tiles_n = 0;
+  bool single_wg = false;      // whole update per matrix in one workgroup (small shapes)
   double work = 0.0;
 };
 
@@ -168,6 +169,16 @@ int heuristic_apply(int64_t Mp, int64_t Np, int64_t count, int cu, bool f32) {
   return (2 * t128 * count >= cu) ? TILE_128 : TILE_64;
 }
 
+// Small shapes on the bf16 path can run their whole update in one workgroup per matrix
+// (small.hip): padded m' <= 128 and m' n' <= 64 Ki elements, so U fits in one workgroup's
+// LDS. One launch then replaces the ~20 of the staged path, which wins when the list holds
+// only such shapes. Beside larger groups the staged launches of the small groups fill the
+// gaps of the larger groups' launches on their own streams, while single-workgroup
+// kernels (one workgroup per CU for their whole duration) delay them; measured on the
+// 832-matrix list: 0.72 ms staged, 0.77-0.80 ms with single-workgroup small groups. So a
+// list uses the kernel only when every group qualifies.
+bool single_wg_shape(int64_t Mp, int64_t Np) { return Mp <= 128 && Mp * Np <= kSmallMaxElems; }
+
 int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams& hp,
                bool need_ptrs, Plan& plan) {
   plan = Plan{};
@@ -197,6 +208,15 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
       (void)nt_sq;
       g.work = kernel_flops(m, n, g.mode, hp) * cnt;
       plan.groups.push_back(std::move(g));
+    }
+  }
+  bool all_small = !f32 && !(ctx->flags & MUON_FLAG_STAGED_ONLY);
+  for (const Group& g : plan.groups) all_small = all_small && single_wg_shape(g.Mp, g.Np);
+  if (all_small) {
+    for (Group& g : plan.groups) {
+      g.single_wg = true;
+      g.tile_sq = g.tile_ap = -1;
+      g.work = dense_flops(g.m, g.n, g.mode, hp) * static_cast<double>(g.members.size());
     }
   }
   // Largest work first: the big launches start while the host still enqueues the rest.
@@ -248,9 +268,9 @@ struct StepEnv {
 // One stage name per kernel symbol: "syrk_u" is the Gram product of the momentum output
 // (bf16 operands on the bf16 path), "syrk" the one of the fp16 / fp32 iterate.
 constexpr const char* kStageNames[] = {"table", "momentum", "norm_finalize", "transpose", "syrk",
-                                       "square", "apply", "apply_update", "syrk_u"};
+                                       "square", "apply", "apply_update", "syrk_u", "single_wg"};
 enum Stage { ST_TABLE, ST_MOMENTUM, ST_FINALIZE, ST_TRANSPOSE, ST_SYRK, ST_SQUARE, ST_APPLY, ST_UPDATE,
-             ST_SYRK_U };
+             ST_SYRK_U, ST_SINGLE_WG };
 constexpr size_t kMaxRecords = 1 << 16;
 
 // Brackets one launch with events when profiling is on (no effect otherwise).
@@ -463,7 +483,7 @@ hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* 
 // context does not measure): such a group makes no host synchronisation and may run on
 // a stream of its own next to other groups.
 bool group_tuned(const muon_ctx* ctx, const Group& g, const muon_hparams& hp, bool f32) {
-  if (ctx->flags & MUON_FLAG_MODEL_ONLY) return true;
+  if ((ctx->flags & MUON_FLAG_MODEL_ONLY) || g.single_wg) return true;
   const int rounds = total_rounds(hp);
   const bool more = (g.mode == MUON_NS_PLAIN) ? rounds > 1 : hp.n_segments > 1;
   const int cnt = static_cast<int>(g.members.size());
@@ -507,6 +527,36 @@ int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
   void* XT[2] = {env.ws + g.off_xt[0], env.ws + g.off_xt[1]};
   const int count = static_cast<int32_t>(g.members.size());
   float* s = reinterpret_cast<float*>(env.ws + g.off_s);
+
+  if (g.single_wg) {
+    SmallParams sp;
+    std::memset(&sp, 0, sizeof(sp));
+    sp.table = table;
+    sp.count = count;
+    sp.m = static_cast<int32_t>(g.m); sp.n = static_cast<int32_t>(g.n);
+    sp.Mp = static_cast<int32_t>(g.Mp); sp.Np = static_cast<int32_t>(g.Np);
+    sp.X = X; sp.XT[0] = XT[0]; sp.XT[1] = XT[1];
+    const int nsq = (g.mode == MUON_NS_GRAM) ? 4 : 2;
+    for (int k = 0; k < nsq; ++k) sp.S[k] = env.ws + g.off_sq[k];
+    sp.sX = g.stride_x; sp.sXT = g.stride_x; sp.sS = g.stride_sq;
+    sp.mu = hp.momentum; sp.eps = hp.eps; sp.lr = hp.lr; sp.wd = hp.weight_decay;
+    sp.a = hp.a; sp.b = hp.b; sp.c = hp.c;
+    sp.xs = pow2_near(std::sqrt(static_cast<double>(g.m) * g.n), 0, 14);
+    sp.e = pow2_near(static_cast<double>(g.m), 0, 14);
+    sp.nesterov = hp.nesterov;
+    sp.plain = g.mode == MUON_NS_PLAIN;
+    sp.rounds = total_rounds(hp);
+    sp.n_segments = hp.n_segments;
+    for (int k = 0; k < hp.n_segments; ++k) sp.segments[k] = hp.segments[k];
+    sp.g_bf16 = hp.g_dtype == MUON_BF16; sp.m_bf16 = hp.m_dtype == MUON_BF16; sp.w_bf16 = hp.w_dtype == MUON_BF16;
+    const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;
+    const double wb = hp.w_dtype == MUON_BF16 ? 2.0 : 4.0;
+    StageTimer tm(env.ctx, env.st, ST_SINGLE_WG, g.m, g.n, count, dense_flops(g.m, g.n, g.mode, hp) * count,
+                  static_cast<double>(count) * g.m * g.n * (gb + 2.0 * mb + 2.0 * wb));
+    MUON_HIP(launch_small_ns(sp, env.st));
+    tm.done();
+    return MUON_OK;
+  }
 
   // Momentum, canonical U (into X) and per-tile partial sums of squares.
   MomentumParams mp;
@@ -641,7 +691,7 @@ int muon_init(muon_ctx** out, int device, uint32_t flags) {
   try {
     if (!out) return MUON_ERR_ARG;
     *out = nullptr;
-    if ((flags & ~(MUON_FLAG_MODEL_ONLY | MUON_FLAG_PROFILE)) != 0) return MUON_ERR_ARG;
+    if ((flags & ~(MUON_FLAG_MODEL_ONLY | MUON_FLAG_PROFILE | MUON_FLAG_STAGED_ONLY)) != 0) return MUON_ERR_ARG;
     if (device == -1) {  // host-only context: planning and validation, no launches
       muon_ctx* c = new (std::nothrow) muon_ctx;
       if (!c) return MUON_ERR_HIP;
@@ -848,8 +898,8 @@ int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon
     out->group = plan.group_of[index];
     out->tile_sym = g.tile_sq;
     out->tile_apply = g.tile_ap;
-    out->reserved = 0;
-    if (!(ctx->flags & MUON_FLAG_MODEL_ONLY)) {
+    out->single_wg = g.single_wg ? 1 : 0;
+    if (!g.single_wg && !(ctx->flags & MUON_FLAG_MODEL_ONLY)) {
       const int f32 = hp->ns_dtype == MUON_F32 ? 1 : 0;
       const int cnt = static_cast<int>(g.members.size());
       std::lock_guard<std::mutex> lk(g_tune_mu);
@@ -859,7 +909,7 @@ int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon
       if (b != g_tuned.end()) out->tile_apply = b->second;
     }
     out->dense_flops = dense_flops(g.m, g.n, g.mode, *hp);
-    out->kernel_flops = kernel_flops(g.m, g.n, g.mode, *hp);
+    out->kernel_flops = g.single_wg ? out->dense_flops : kernel_flops(g.m, g.n, g.mode, *hp);
     return MUON_OK;
   } catch (...) {
     return MUON_ERR_HIP;

@@ -131,6 +131,28 @@ hipError_t launch_transpose_scale(const TransposeParams& p, hipStream_t st);
 hipError_t launch_norm_finalize(const float* partials, int per_matrix, int count, float eps,
                                 float* s, hipStream_t st);
 
+// The whole update of each matrix of a small same-shape group in one workgroup (bf16 path,
+// padded m' <= 128 and m' n' <= kSmallMaxElems): momentum, norm, the NS schedule (plain rounds or Gram segments) and the W
+// update. Buffers are the group's workspace: X (Mp x Np), XT[2] (Np x Mp), S[0..3] (Mp x Mp;
+// S[2], S[3] unused by plain NS), matrix i at base + i * stride (elements).
+struct SmallParams {
+  const MatDesc* table;
+  int32_t count;
+  int32_t m, n, Mp, Np;
+  void* X; void* XT[2]; void* S[4];
+  int64_t sX, sXT, sS;
+  float mu, eps, lr, wd;
+  float a, b, c;
+  float xs, e;               // iterate scale (fp16 X = xs * X), Gram-space scale
+  int32_t nesterov;
+  int32_t plain, rounds;     // plain NS with `rounds` rounds, else Gram segments
+  int32_t n_segments;
+  int32_t segments[8];
+  int32_t g_bf16, m_bf16, w_bf16;
+};
+hipError_t launch_small_ns(const SmallParams& p, hipStream_t st);
+constexpr int kSmallMaxElems = 64 * 1024;  // padded m' n' the single-workgroup kernel takes
+
 // Copy up to kTableChunk descriptors (passed by value) into device memory.
 constexpr int kTableChunk = 48;
 struct TableChunk {

@@ -117,7 +117,7 @@ def test_profile_read_errors(hctx):
 def test_init_errors():
     out = ctypes.c_void_p()
     assert B._lib.muon_init(None, 0, 0) == B.MUON_ERR_ARG
-    assert B._lib.muon_init(ctypes.byref(out), -1, 4) == B.MUON_ERR_ARG
+    assert B._lib.muon_init(ctypes.byref(out), -1, 8) == B.MUON_ERR_ARG
     assert B._lib.muon_init(ctypes.byref(out), 9999, 0) == B.MUON_ERR_DEVICE
     assert B._lib.muon_destroy(None) == B.MUON_OK
 
@@ -188,13 +188,31 @@ def test_plan_flops_match_oracle_model(hctx):
     for segs in [(2, 2, 1), (2, 3), (1, 1, 1, 1, 1), (5,), (3, 1, 1)]:
         for mode in ("plain", "gram"):
             for (r, c), e in zip(shapes, plan(hctx, shapes, segments=segs, mode=mode)):
+                assert e.single_wg == 0   # a list with large shapes stays on the staged kernels
                 assert e.mode == B.MODES[mode]
                 assert e.dense_flops == pytest.approx(flop_model.dense_flops(r, c, mode, segs), rel=1e-12)
                 m, n = min(r, c), max(r, c)
                 assert (e.m, e.n, e.transposed) == (m, n, int(r > c))
-                # symmetric outputs computed once: SYRK m'^2 n', squares m'^3, apply 2 m'^2 n'
                 nl, ns = flop_model.product_counts(mode, segs)
+                # symmetric outputs computed once: SYRK m'^2 n', squares m'^3, apply 2 m'^2 n'
                 assert e.kernel_flops == pytest.approx((nl // 2) * 3.0 * m * m * n + ns * 1.0 * m ** 3, rel=1e-12)
+
+
+def test_single_workgroup_choice(hctx):
+    """Lists of small shapes only (padded m' <= 128, m' n' <= 64 Ki) run one workgroup per
+    matrix, computing every product densely; one larger shape keeps the list staged."""
+    small = [(64, 256), (300, 70), (1, 17), (128, 512), (1024, 64)]
+    for i, e in enumerate(plan(hctx, small)):
+        assert e.single_wg == 1 and (e.tile_sym, e.tile_apply) == (-1, -1)
+        assert e.kernel_flops == pytest.approx(e.dense_flops, rel=1e-12)
+    for extra in [(129, 512), (128, 576), (64, 1088)]:
+        assert all(e.single_wg == 0 for e in plan(hctx, small + [extra]))
+    staged = B.muon_init(-1, B.MUON_FLAG_STAGED_ONLY)
+    try:
+        assert all(e.single_wg == 0 for e in plan(staged, small))
+    finally:
+        B.muon_destroy(staged)
+    assert all(e.single_wg == 0 for e in plan(hctx, small, ns_dtype="f32", g_dtype="f32", m_dtype="f32"))
 
 
 def test_auto_dispatch_follows_flop_model(hctx):

@@ -192,6 +192,54 @@ def test_small_batch_832_full(B, ctx):
     check_step(B, ctx, w, mode="gram", gpu_mode="auto")
 
 
+@pytest.fixture(scope="module")
+def ctx_staged(B):
+    c = B.muon_init(0, B.MUON_FLAG_STAGED_ONLY)
+    yield c
+    B.muon_destroy(c)
+
+
+@pytest.mark.parametrize("mode", ["gram", "plain"])
+def test_small_shapes_both_paths(B, ctx, ctx_staged, mode):
+    """Shapes the single-workgroup kernel takes (padded m' <= 128 and m' n' <= 64 Ki; 1 x 17
+    up to 128 x 512 and 64 x 1024, tall and wide, ragged), on it and on the staged kernels: both within the bar of the oracle, over
+    two steps with momentum carried."""
+    shapes = [(1, 17), (64, 256), (256, 64), (100, 300), (65, 500), (128, 128), (7, 129), (128, 512),
+              (64, 1024), (1000, 60)]
+    # i.i.d. gradients as in the small-matrix workload (a rank-4 gradient plus 1% noise on
+    # these shapes puts the bf16 rounding of U above the bar on both paths alike)
+    w = wl.custom("small_both", shapes, structure="gaussian", wid=213, steps=2)
+    hp = B.make_hparams(mode=mode)
+    raw = [(0, 0, 0, r, c) for r, c in shapes]
+    assert all(B.muon_plan_info(ctx, raw, hp, i).single_wg == 1 for i in range(len(shapes)))
+    assert all(B.muon_plan_info(ctx_staged, raw, hp, i).single_wg == 0 for i in range(len(shapes)))
+    e1 = check_step(B, ctx, w, mode=mode, steps=2)
+    e2 = check_step(B, ctx_staged, w, mode=mode, steps=2)
+    assert e1 <= 2e-2 and e2 <= 2e-2
+
+
+@pytest.mark.parametrize("segments", [(2, 3), (1, 1, 1, 1, 1), (4,)])
+def test_small_shapes_schedules(B, ctx, segments):
+    w = wl.custom("small_sched", [(96, 320), (128, 512)], structure="gaussian", wid=214)
+    check_step(B, ctx, w, mode="gram", segments=segments)
+
+
+def test_small_bf16_weights(B, ctx):
+    w = wl.custom("small_bf16w", [(64, 256), (300, 70)], structure="gaussian", wid=215)
+    w = wl.Workload(**{**w.__dict__, "w_dtype": "bf16"})
+    st = GpuState(w)
+    st.load_gradients(0)
+    run_step(ctx, st, B.make_hparams(w_dtype="bf16", mode="gram"))
+    for k in range(2):
+        W0 = wl.weight_np(w, k).astype(np.float64)
+        G = wl.gradient_np(w, 0, k).astype(np.float64)
+        W_ref, _, _ = om.muon_step(W0, G, np.zeros_like(W0), mode="gram")
+        W_gpu = to_np(st.W[k])
+        step = np.abs(W_ref - W0).max()
+        assert np.all(np.abs(W_gpu - W_ref) <= 2.0 ** -9 * np.abs(W_ref) + 0.05 * step)
+        assert rel(W_gpu - W0, W_ref - W0) < 0.1
+
+
 # ---------------------------------------------------------------- edge cases
 
 def test_zero_gradient_and_determinism(B, ctx):

@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--details", action="store_true", help="also print the per-stage table to stderr")
+    ap.add_argument("--mode", default="auto", choices=["auto", "gram", "plain", "auto_schedule"],
+                    help="NS form: auto (plain or Gram 2+2+1 per shape, the default), gram, plain, or "
+                         "auto_schedule (plain or Gram with the cheapest segment count per shape)")
     ap.add_argument("--tune-cache", default=None,
                     help="tile-choice file: loaded before the warmup when it exists, written after "
                          "it (so that separate profiling runs use the same kernels)")
@@ -150,7 +153,7 @@ def main():
           file=sys.stderr, flush=True)
     Ws, Gs, Ms, data = make_inputs(w, torch)
     mats = list(zip(Ws, Gs, Ms))
-    hp = B.make_hparams(lr=w.lr, momentum=w.mu, weight_decay=w.wd, mode="auto",
+    hp = B.make_hparams(lr=w.lr, momentum=w.mu, weight_decay=w.wd, mode=args.mode,
                         w_dtype=w.w_dtype, g_dtype=w.g_dtype, m_dtype=w.m_dtype, ns_dtype=w.ns_dtype)
     ctx = B.muon_init(0)
     pctx = B.muon_init(0, B.MUON_FLAG_PROFILE)
@@ -240,7 +243,10 @@ def main():
         "data": f"synthetic ({data})",
         "config": {"workload": w.name, "matrices": len(w.matrices), "elements": w.elements,
                    "shapes": sorted({f"{s.rows}x{s.cols}" for s in w.matrices}),
-                   "ns": "auto (FLOP-model dispatch: Gram 2+2+1 or plain 5 rounds)",
+                   "ns": {"auto": "auto (FLOP-model dispatch: Gram 2+2+1 or plain 5 rounds)",
+                          "gram": "Gram 2+2+1", "plain": "plain 5 rounds",
+                          "auto_schedule": "auto_schedule (plain or Gram with k balanced segments, "
+                                           "5 rounds, per shape by measured stage times)"}[args.mode],
                    "storage": {"W": w.w_dtype, "G": w.g_dtype, "M": w.m_dtype}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": None,
@@ -263,7 +269,7 @@ def main():
             continue
         e = B.muon_plan_info(ctx, mats, hp, i)
         plans[key] = {"mode": {1: "plain", 2: "gram"}[e.mode], "tile_sym": e.tile_sym,
-                      "tile_apply": e.tile_apply}
+                      "tile_apply": e.tile_apply, "segments": list(e.segments[:e.n_segments])}
     out["config"]["plan"] = plans
     rec = traffic_record(w.name)
     st = rec["kernels"].get(f"{dom['stage']}/{dom['tile']}") if rec else None

@@ -48,6 +48,7 @@ extern "C" {
 #define MUON_NS_AUTO 0   /* per shape: the dispatcher picks plain or Gram */
 #define MUON_NS_PLAIN 1  /* sum(segments) plain rounds (segments ignored otherwise) */
 #define MUON_NS_GRAM 2   /* Gram-space NS with the given segments */
+#define MUON_NS_AUTO_SCHEDULE 3  /* per shape: plain NS or Gram NS with k segments, chosen below */
 
 #define MUON_MAX_SEGMENTS 8
 
@@ -76,8 +77,20 @@ typedef struct muon_matrix {
  *   nesterov:           0 or 1
  *   a, b, c:            quintic NS coefficients (finite)
  *   n_segments, segments[]: 1..MUON_MAX_SEGMENTS segments, each >= 1; their sum is the
- *                       number of NS rounds (at most 64)
- *   mode:               MUON_NS_AUTO | MUON_NS_PLAIN | MUON_NS_GRAM
+ *                       number of NS rounds (at most 64). With ns_dtype MUON_BF16 a Gram
+ *                       segment longer than 3 rounds returns MUON_ERR_UNSUPPORTED: the
+ *                       fp16 Gram-space recurrence loses the small singular directions
+ *                       of low-rank inputs from the fourth round on.
+ *   mode:               MUON_NS_AUTO | MUON_NS_PLAIN | MUON_NS_GRAM | MUON_NS_AUTO_SCHEDULE
+ *                       AUTO_SCHEDULE (MuonX article, section 3.2: the best segment split
+ *                       depends on shape and precision): every Gram segmentation of the
+ *                       R = sum(segments) rounds, like plain NS, reaches the same result in
+ *                       exact arithmetic, so per shape the cheapest is run: plain NS or Gram
+ *                       NS with k balanced segments (longer ones first, each at most 3
+ *                       rounds on the bf16 path). A Gram segment count k costs k SYRK and k
+ *                       apply products plus 4R - 3k m'xm' products, plain NS R of each; the
+ *                       costs are the measured times of the shape's stages once a step has
+ *                       measured its tiles, else the FLOP counts the kernels perform.
  *   w_dtype:            MUON_F32 or MUON_BF16
  *   g_dtype, m_dtype:   MUON_F32 or MUON_BF16
  *   ns_dtype:           MUON_BF16: bf16 iterate with fp32-accumulate MFMA, the m'xm'
@@ -101,6 +114,9 @@ typedef struct muon_hparams {
 /* Per-matrix plan as chosen by the dispatcher (muon_plan_info). */
 typedef struct muon_plan_entry {
   int32_t mode;          /* MUON_NS_PLAIN or MUON_NS_GRAM actually used */
+  int32_t n_segments;    /* the schedule used: Gram segments, or the rounds of plain NS as
+                            one entry */
+  int32_t segments[MUON_MAX_SEGMENTS];
   int32_t transposed;    /* 1 if rows > cols (processed as the transpose) */
   int64_t m, n;          /* canonical short side m' and long side n' */
   int32_t group;         /* same-shape group index (one batched launch per stage) */

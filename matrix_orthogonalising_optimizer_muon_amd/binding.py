@@ -38,13 +38,15 @@ MUON_BF16 = 1
 MUON_NS_AUTO = 0
 MUON_NS_PLAIN = 1
 MUON_NS_GRAM = 2
+MUON_NS_AUTO_SCHEDULE = 3
 MUON_MAX_SEGMENTS = 8
 MUON_FLAG_MODEL_ONLY = 1
 MUON_FLAG_PROFILE = 2
 MUON_FLAG_STAGED_ONLY = 4
 
 DTYPES = {"f32": MUON_F32, "bf16": MUON_BF16}
-MODES = {"auto": MUON_NS_AUTO, "plain": MUON_NS_PLAIN, "gram": MUON_NS_GRAM}
+MODES = {"auto": MUON_NS_AUTO, "plain": MUON_NS_PLAIN, "gram": MUON_NS_GRAM,
+         "auto_schedule": MUON_NS_AUTO_SCHEDULE}
 
 
 class muon_matrix(ctypes.Structure):
@@ -63,7 +65,8 @@ class muon_hparams(ctypes.Structure):
 
 
 class muon_plan_entry(ctypes.Structure):
-    _fields_ = [("mode", ctypes.c_int32), ("transposed", ctypes.c_int32),
+    _fields_ = [("mode", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+                ("segments", ctypes.c_int32 * MUON_MAX_SEGMENTS), ("transposed", ctypes.c_int32),
                 ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("group", ctypes.c_int32),
                 ("tile_sym", ctypes.c_int32), ("tile_apply", ctypes.c_int32),
                 ("single_wg", ctypes.c_int32), ("dense_flops", ctypes.c_double),

@@ -57,7 +57,14 @@ namespace {
 constexpr int64_t kPad = 64;          // canonical dims are padded to multiples of 64
 constexpr int64_t kMaxDim = 1 << 20;  // per-dimension limit
 constexpr int kMaxRounds = 64;
-constexpr int kMaxBf16Segment = 8;    // fp16 transform: a^k must stay far below 65504
+// Longest Gram segment on the bf16 path. The fp16 recurrence mixes eigenvalues that the
+// iteration drives apart (large directions settle near 1/sigma, small ones grow as a^k)
+// in one fp16 matrix; from 4 rounds on the small directions are lost. Measured against
+// the fp64 oracle: a 512 x 2048 rank-16 gradient gives errors 3e-3 to 4e-3 with
+// [2,2,1], [2,3] and [3,2], but 2e3 with [4,1] and inf with [5]; a 2560 x 9728 one 4e-2
+// with [5]. Three rounds is also the longest segment of the open-source fp16 default
+// 2 + 3 (MuonX article, section 3.2).
+constexpr int kMaxBf16Segment = 3;
 constexpr int kMaxBatch = 65535;      // grid.y limit per launch
 constexpr size_t kAlign = 256;
 
@@ -79,6 +86,7 @@ struct Group {
   int mom_tiles_m = 0, mom_tiles_n = 0;
   bool single_wg = false;      // whole update per matrix in one workgroup (small shapes)
   double work = 0.0;
+  muon_hparams hs{};           // the call's hparams with this group's mode and schedule
 };
 
 struct Plan {
@@ -103,10 +111,12 @@ int validate_hparams(const muon_hparams* hp) {
     rounds += hp->segments[i];
   }
   if (rounds > kMaxRounds) return MUON_ERR_ARG;
-  if (hp->mode != MUON_NS_AUTO && hp->mode != MUON_NS_PLAIN && hp->mode != MUON_NS_GRAM) return MUON_ERR_ARG;
+  if (hp->mode != MUON_NS_AUTO && hp->mode != MUON_NS_PLAIN && hp->mode != MUON_NS_GRAM &&
+      hp->mode != MUON_NS_AUTO_SCHEDULE)
+    return MUON_ERR_ARG;
   for (int dt : {hp->w_dtype, hp->g_dtype, hp->m_dtype, hp->ns_dtype})
     if (dt != MUON_F32 && dt != MUON_BF16) return MUON_ERR_ARG;
-  if (hp->ns_dtype == MUON_BF16 && hp->mode != MUON_NS_PLAIN) {
+  if (hp->ns_dtype == MUON_BF16 && hp->mode != MUON_NS_PLAIN && hp->mode != MUON_NS_AUTO_SCHEDULE) {
     for (int i = 0; i < hp->n_segments; ++i)
       if (hp->segments[i] > kMaxBf16Segment) return MUON_ERR_UNSUPPORTED;
   }
@@ -150,7 +160,7 @@ double kernel_flops(int64_t m, int64_t n, int mode, const muon_hparams& hp) {
 // Shape-adaptive choice of the NS form: Gram pays when the long products it saves cost
 // more than the square ones it adds (MuonX section 3.2: benefit depends on the shape).
 int choose_mode(int64_t m, int64_t n, const muon_hparams& hp) {
-  if (hp.mode != MUON_NS_AUTO) return hp.mode;
+  if (hp.mode != MUON_NS_AUTO) return hp.mode;  // AUTO_SCHEDULE is resolved per group later
   return dense_flops(m, n, MUON_NS_GRAM, hp) < dense_flops(m, n, MUON_NS_PLAIN, hp) ? MUON_NS_GRAM
                                                                                       : MUON_NS_PLAIN;
 }
@@ -168,6 +178,8 @@ int heuristic_apply(int64_t Mp, int64_t Np, int64_t count, int cu, bool f32) {
   const int64_t t128 = ((Mp + 127) / 128) * ((Np + 127) / 128);
   return (2 * t128 * count >= cu) ? TILE_128 : TILE_64;
 }
+
+void choose_schedule(const muon_ctx* ctx, Group& g, const muon_hparams& hp, bool f32);
 
 // Small shapes on the bf16 path can run their whole update in one workgroup per matrix
 // (small.hip): padded m' <= 128 and m' n' <= 64 Ki elements, so U fits in one workgroup's
@@ -199,14 +211,15 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
       Group g;
       g.m = m; g.n = n;
       g.Mp = round_up(m, kPad); g.Np = round_up(n, kPad);
-      g.mode = choose_mode(m, n, hp);
       g.members.assign(all.begin() + b, all.begin() + std::min(all.size(), b + kMaxBatch));
       const int64_t cnt = static_cast<int64_t>(g.members.size());
-      const int64_t nt_sq = (g.Mp + 127) / 128;
+      g.hs = hp;
+      if (hp.mode == MUON_NS_AUTO_SCHEDULE) choose_schedule(ctx, g, hp, f32);
+      else g.mode = choose_mode(m, n, hp);
+      g.hs.mode = g.mode;
       g.tile_sq = heuristic_sym(g.Mp, cnt, ctx->cu_count);
       g.tile_ap = heuristic_apply(g.Mp, g.Np, cnt, ctx->cu_count, f32);
-      (void)nt_sq;
-      g.work = kernel_flops(m, n, g.mode, hp) * cnt;
+      g.work = kernel_flops(m, n, g.mode, g.hs) * cnt;
       plan.groups.push_back(std::move(g));
     }
   }
@@ -216,7 +229,7 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
     for (Group& g : plan.groups) {
       g.single_wg = true;
       g.tile_sq = g.tile_ap = -1;
-      g.work = dense_flops(g.m, g.n, g.mode, hp) * static_cast<double>(g.members.size());
+      g.work = dense_flops(g.m, g.n, g.mode, g.hs) * static_cast<double>(g.members.size());
     }
   }
   // Largest work first: the big launches start while the host still enqueues the rest.
@@ -337,6 +350,43 @@ void set_sym_tiles(GemmParams& p, int64_t Mp, int cfg) {
 using TuneKey = std::tuple<int, int, int, int64_t, int64_t, int>;
 std::mutex g_tune_mu;
 std::map<TuneKey, int> g_tuned;
+std::map<TuneKey, float> g_tuned_ms;   // measured time of the chosen configuration
+
+// MUON_NS_AUTO_SCHEDULE: plain NS or Gram NS with k balanced segments, whichever costs
+// least for the group's shape. Costs per product kind are the measured times of the
+// shape's Gram product, m' x m' product and apply when a step has measured their tiles,
+// else the FLOPs the kernels perform (m'^2 n', m'^3 and 2 m'^2 n'). Ties keep plain NS,
+// then the larger k.
+void choose_schedule(const muon_ctx* ctx, Group& g, const muon_hparams& hp, bool f32) {
+  const int R = total_rounds(hp);
+  const int cap = f32 ? kMaxRounds : kMaxBf16Segment;
+  double ts = 1.0 * g.m * g.m * g.n, ta = 2.0 * g.m * g.m * g.n, tq = 1.0 * g.m * g.m * g.m;
+  if (!(ctx->flags & MUON_FLAG_MODEL_ONLY)) {
+    const int cnt = static_cast<int>(g.members.size());
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    auto s = g_tuned_ms.find(std::make_tuple(ctx->device, static_cast<int>(OP_SYRK_IN), f32 ? 1 : 0, g.Mp, g.Mp, cnt));
+    auto q = g_tuned_ms.find(std::make_tuple(ctx->device, static_cast<int>(OP_SYM), f32 ? 1 : 0, g.Mp, g.Mp, cnt));
+    auto a = g_tuned_ms.find(std::make_tuple(ctx->device, static_cast<int>(OP_APPLY), f32 ? 1 : 0, g.Mp, g.Np, cnt));
+    if (s != g_tuned_ms.end() && q != g_tuned_ms.end() && a != g_tuned_ms.end()) {
+      ts = s->second; tq = q->second; ta = a->second;
+    }
+  }
+  double best = R * (ts + tq + ta);
+  int best_k = 0;  // plain
+  const int kmin = (R + cap - 1) / cap, kmax = std::min(R, MUON_MAX_SEGMENTS);
+  for (int k = kmax; k >= kmin; --k) {
+    const double cost = k * (ts + ta) + (4.0 * R - 3.0 * k) * tq;
+    if (cost < best * (1.0 - 1e-9)) { best = cost; best_k = k; }
+  }
+  if (best_k == 0) {
+    g.mode = MUON_NS_PLAIN;
+    return;
+  }
+  g.mode = MUON_NS_GRAM;
+  g.hs.n_segments = best_k;
+  for (int i = 0; i < MUON_MAX_SEGMENTS; ++i) g.hs.segments[i] = 0;
+  for (int i = 0; i < best_k; ++i) g.hs.segments[i] = R / best_k + (i < R % best_k ? 1 : 0);
+}
 
 template <class Build>
 hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristic, bool sym,
@@ -389,10 +439,12 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
         }
       }
       const float best = *std::min_element(times.begin(), times.end());
+      float chosen = best;
       for (size_t ci = 0; ci < cands.size(); ++ci)
-        if (times[ci] <= best * 1.02f) { cfg = cands[ci]; break; }
+        if (times[ci] <= best * 1.02f) { cfg = cands[ci]; chosen = times[ci]; break; }
       std::lock_guard<std::mutex> lk(g_tune_mu);
       g_tuned[key] = cfg;
+      g_tuned_ms[key] = chosen;
     }
   }
   const GemmParams p = build(cfg);
@@ -484,8 +536,9 @@ hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* 
 // a stream of its own next to other groups.
 bool group_tuned(const muon_ctx* ctx, const Group& g, const muon_hparams& hp, bool f32) {
   if ((ctx->flags & MUON_FLAG_MODEL_ONLY) || g.single_wg) return true;
-  const int rounds = total_rounds(hp);
-  const bool more = (g.mode == MUON_NS_PLAIN) ? rounds > 1 : hp.n_segments > 1;
+  (void)hp;
+  const int rounds = total_rounds(g.hs);
+  const bool more = (g.mode == MUON_NS_PLAIN) ? rounds > 1 : g.hs.n_segments > 1;
   const int cnt = static_cast<int>(g.members.size());
   std::vector<TuneKey> keys = {
       std::make_tuple(ctx->device, static_cast<int>(OP_SYRK_IN), f32 ? 1 : 0, g.Mp, g.Mp, cnt),
@@ -521,7 +574,7 @@ bool ensure_lanes(muon_ctx* ctx, int n) {
 }
 
 int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
-  const muon_hparams& hp = *env.hp;
+  const muon_hparams& hp = g.hs;   // the group's mode and schedule
   const bool f32 = env.f32;
   void* X = env.ws + g.off_x;
   void* XT[2] = {env.ws + g.off_xt[0], env.ws + g.off_xt[1]};
@@ -908,8 +961,16 @@ int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon
       auto b = g_tuned.find(std::make_tuple(ctx->device, static_cast<int>(OP_APPLY), f32, g.Mp, g.Np, cnt));
       if (b != g_tuned.end()) out->tile_apply = b->second;
     }
-    out->dense_flops = dense_flops(g.m, g.n, g.mode, *hp);
-    out->kernel_flops = g.single_wg ? out->dense_flops : kernel_flops(g.m, g.n, g.mode, *hp);
+    out->dense_flops = dense_flops(g.m, g.n, g.mode, g.hs);
+    out->kernel_flops = g.single_wg ? out->dense_flops : kernel_flops(g.m, g.n, g.mode, g.hs);
+    std::memset(out->segments, 0, sizeof(out->segments));
+    if (g.mode == MUON_NS_PLAIN) {
+      out->n_segments = 1;
+      out->segments[0] = total_rounds(g.hs);
+    } else {
+      out->n_segments = g.hs.n_segments;
+      for (int k = 0; k < g.hs.n_segments; ++k) out->segments[k] = g.hs.segments[k];
+    }
     return MUON_OK;
   } catch (...) {
     return MUON_ERR_HIP;

@@ -145,9 +145,12 @@ def test_validation_before_device(hctx):
         if kw.get("segments") == []:
             hp.n_segments = 0
         assert step(hctx, ok_shapes, hp) == B.MUON_ERR_ARG, kw
-    # fp16 transform limit: a Gram segment longer than 8 rounds on the bf16 path
-    assert step(hctx, ok_shapes, B.make_hparams(segments=[9], mode="gram")) == B.MUON_ERR_UNSUPPORTED
+    # fp16 Gram-space limit: a Gram segment longer than 3 rounds on the bf16 path
+    assert step(hctx, ok_shapes, B.make_hparams(segments=[4, 1], mode="gram")) == B.MUON_ERR_UNSUPPORTED
+    assert step(hctx, ok_shapes, B.make_hparams(segments=[4, 1], mode="auto")) == B.MUON_ERR_UNSUPPORTED
+    assert step(hctx, ok_shapes, B.make_hparams(segments=[3, 2], mode="gram")) == B.MUON_ERR_DEVICE
     assert step(hctx, ok_shapes, B.make_hparams(segments=[9], mode="plain")) == B.MUON_ERR_DEVICE
+    assert step(hctx, ok_shapes, B.make_hparams(segments=[9], mode="auto_schedule")) == B.MUON_ERR_DEVICE
     assert step(hctx, ok_shapes, B.make_hparams(segments=[9], mode="gram", ns_dtype="f32")) == B.MUON_ERR_DEVICE
 
 
@@ -186,8 +189,10 @@ def plan(hctx, shapes, **kw):
 def test_plan_flops_match_oracle_model(hctx):
     shapes = [(2560, 9728), (9728, 2560), (64, 256), (300, 70), (2048, 2048), (512, 3584)]
     for segs in [(2, 2, 1), (2, 3), (1, 1, 1, 1, 1), (5,), (3, 1, 1)]:
+        # segments longer than 3 rounds exist on the fp32 path only
+        dt = dict(ns_dtype="f32", g_dtype="f32", m_dtype="f32") if max(segs) > 3 else {}
         for mode in ("plain", "gram"):
-            for (r, c), e in zip(shapes, plan(hctx, shapes, segments=segs, mode=mode)):
+            for (r, c), e in zip(shapes, plan(hctx, shapes, segments=segs, mode=mode, **dt)):
                 assert e.single_wg == 0   # a list with large shapes stays on the staged kernels
                 assert e.mode == B.MODES[mode]
                 assert e.dense_flops == pytest.approx(flop_model.dense_flops(r, c, mode, segs), rel=1e-12)
@@ -286,3 +291,57 @@ def test_tune_cache_rejects_bad_files(hctx, tmp_path, text):
     assert B.muon_plan_info(hctx, [(0, 0, 0, 640, 1280)] * 3, B.make_hparams(), 0).tile_apply == before
     with pytest.raises(B.MuonError):
         B.muon_tune_load(hctx, str(tmp_path / "missing.txt"))
+
+
+# ---------------------------------------------------------------- per-shape schedule
+
+def _expected_schedule(m, n, R, cap=3):
+    """Cheapest of plain NS and Gram NS with k balanced segments (longer first), counted
+    with the oracle's product counts and the kernels' cost per product (Gram product
+    m'^2 n', apply 2 m'^2 n', m' x m' product m'^3); ties keep plain, then the larger k."""
+    def cost(mode, segs):
+        n_long, n_sq = flop_model.product_counts(mode, segs, rounds=R if mode == "plain" else None)
+        return (n_long // 2) * (1.0 * m * m * n + 2.0 * m * m * n) + n_sq * 1.0 * m ** 3
+    best, choice = cost("plain", (R,)), ("plain", (R,))
+    for k in range(min(R, 8), -(-R // cap) - 1, -1):
+        segs = tuple(R // k + (1 if i < R % k else 0) for i in range(k))
+        c = cost("gram", segs)
+        if c < best * (1 - 1e-9):
+            best, choice = c, ("gram", segs)
+    return choice
+
+
+@pytest.mark.parametrize("segs", [(2, 2, 1), (5,), (1, 1, 1), (3, 4), (4, 4, 4, 4, 4)])
+def test_auto_schedule_model_choice(hctx, segs):
+    shapes = [(2560, 9728), (9728, 2560), (2048, 2048), (512, 3584), (3584, 18944), (300, 70), (1000, 1400)]
+    R = sum(segs)
+    mctx = B.muon_init(-1, B.MUON_FLAG_MODEL_ONLY)
+    try:
+        for (r, c), e in zip(shapes, plan(mctx, shapes, segments=segs, mode="auto_schedule")):
+            m, n = min(r, c), max(r, c)
+            mode, want = _expected_schedule(m, n, R)
+            assert e.mode == B.MODES[mode], ((r, c), segs)
+            got = tuple(e.segments[:e.n_segments])
+            assert got == want, ((r, c), segs, got, want)
+            assert sum(got) == R
+            if mode == "gram":
+                assert max(got) <= 3                      # bf16 path: fp16 Gram-space limit
+                assert e.dense_flops == pytest.approx(flop_model.dense_flops(r, c, "gram", got), rel=1e-12)
+    finally:
+        B.muon_destroy(mctx)
+
+
+def test_auto_schedule_examples(hctx):
+    """Long rectangular shapes take the fewest segments, square ones plain NS."""
+    mctx = B.muon_init(-1, B.MUON_FLAG_MODEL_ONLY)
+    try:
+        e = plan(mctx, [(2560, 9728), (2048, 2048)], mode="auto_schedule")
+        assert (e[0].mode, tuple(e[0].segments[:e[0].n_segments])) == (B.MUON_NS_GRAM, (3, 2))
+        assert (e[1].mode, tuple(e[1].segments[:e[1].n_segments])) == (B.MUON_NS_PLAIN, (5,))
+        e = plan(mctx, [(2560, 9728)], mode="auto_schedule", segments=(4, 4, 4))
+        assert tuple(e[0].segments[:e[0].n_segments]) == (3, 3, 3, 3)
+        e = plan(mctx, [(2560, 9728)], mode="auto_schedule", segments=(4, 4, 4), ns_dtype="f32",
+                 g_dtype="f32", m_dtype="f32")
+        assert tuple(e[0].segments[:e[0].n_segments]) == (12,)
+    finally:
+        B.muon_destroy(mctx)

@@ -146,6 +146,28 @@ def test_bf16_2560x9728_full_size(B, ctx):
     assert e_gram <= 2e-2 and e_plain <= 2e-2
 
 
+def test_bf16_auto_schedule(B, ctx):
+    """Per-shape schedule: plain NS or Gram NS with k balanced segments. Every choice equals
+    plain NS in exact arithmetic, so the oracle's plain update is the reference. Three steps:
+    the first chooses by FLOP count, later ones by the measured stage times."""
+    shapes = [(2560, 9728), (512, 2048), (384, 384), (1024, 256), (96, 700)]
+    w = wl.custom("autosched", shapes, structure="lowrank", rank=16, wid=216, steps=3)
+    check_step(B, ctx, w, mode="plain", gpu_mode="auto_schedule", steps=3)
+    hp = B.make_hparams(mode="auto_schedule")
+    raw = [(0, 0, 0, r, c) for r, c in shapes]
+    for i in range(len(shapes)):
+        e = B.muon_plan_info(ctx, raw, hp, i)
+        assert sum(e.segments[:e.n_segments]) == 5
+
+
+@pytest.mark.parametrize("segments", [(3, 2), (2, 3)])
+def test_bf16_2560x9728_long_segments(B, ctx, segments):
+    """The single long matrix with two Gram segments of 3 and 2 rounds (the schedule the
+    per-shape choice takes for it) against the oracle's plain NS."""
+    w = wl.WORKLOADS["single_bf16_2560x9728"]
+    assert check_step(B, ctx, w, mode="plain", gpu_mode="gram", segments=segments) <= 2e-2
+
+
 @pytest.mark.parametrize("mode", ["gram", "plain"])
 def test_bf16_split_k(B, ctx, mode):
     """Single mid-size matrices: too few tiles for the GPU, so the symmetric stages split K
@@ -218,7 +240,7 @@ def test_small_shapes_both_paths(B, ctx, ctx_staged, mode):
     assert e1 <= 2e-2 and e2 <= 2e-2
 
 
-@pytest.mark.parametrize("segments", [(2, 3), (1, 1, 1, 1, 1), (4,)])
+@pytest.mark.parametrize("segments", [(2, 3), (1, 1, 1, 1, 1), (3, 2), (1, 3, 1)])
 def test_small_shapes_schedules(B, ctx, segments):
     w = wl.custom("small_sched", [(96, 320), (128, 512)], structure="gaussian", wid=214)
     check_step(B, ctx, w, mode="gram", segments=segments)

@@ -240,6 +240,44 @@ int muon_profile_read(muon_ctx *ctx, muon_profile_entry *out, int capacity, int 
 /* Release a context (null is accepted). Work already enqueued is not affected. */
 int muon_destroy(muon_ctx *ctx);
 
+/* ---- AdamW for the parameters Muon does not update ----
+ * MuonX article, section 2: the hidden 2-D weight matrices go to Muon, embeddings, biases
+ * and similar parameters stay with AdamW, which adjusts each element from running
+ * averages of the gradient and of its square. Per element, at step t (1-based):
+ *   W <- W (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+ *   W <- W - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps)
+ * computed in fp32 (decoupled weight decay, bias-corrected moments). */
+typedef struct muon_adamw_tensor {
+  void *W;          /* numel elements in w_dtype, updated in place */
+  const void *G;    /* numel elements in g_dtype, read only */
+  float *m;         /* first moment, fp32, numel elements, updated in place */
+  float *v;         /* second moment, fp32, numel elements, updated in place */
+  int64_t numel;    /* >= 0; 0 skips the tensor (its pointers may then be null) */
+} muon_adamw_tensor;
+
+typedef struct muon_adamw_hparams {
+  float lr;            /* finite */
+  float beta1, beta2;  /* each in [0, 1) */
+  float eps;           /* finite, >= 0 */
+  float weight_decay;  /* finite */
+  int32_t step;        /* t >= 1, for the bias corrections */
+  int32_t w_dtype;     /* MUON_F32 or MUON_BF16 */
+  int32_t g_dtype;     /* MUON_F32 or MUON_BF16 */
+} muon_adamw_hparams;
+
+/* Defaults: lr 1e-3, betas (0.9, 0.999), eps 1e-8, weight_decay 0.01, step 1, W fp32,
+ * G bf16. */
+void muon_adamw_hparams_default(muon_adamw_hparams *hp);
+
+/* One AdamW step over `count` tensors (count == 0 is a no-op), enqueued on `stream`
+ * (asynchronous, no workspace, no host synchronisation). Arrays must not overlap. Every
+ * argument is validated before the first launch (MUON_ERR_ARG: null context or arrays,
+ * negative numel, null pointers of a non-empty tensor, hyper-parameters out of range);
+ * a host-only context returns MUON_ERR_DEVICE after validation. Launch failures return
+ * MUON_ERR_HIP. */
+int muon_adamw_step(muon_ctx *ctx, const muon_adamw_tensor *tensors, int count,
+                    const muon_adamw_hparams *hp, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *muon_status_str(int status);
 

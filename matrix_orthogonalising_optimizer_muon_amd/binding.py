@@ -81,6 +81,17 @@ class muon_profile_entry(ctypes.Structure):
                 ("bytes", ctypes.c_double)]
 
 
+class muon_adamw_tensor(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("G", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+class muon_adamw_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("g_dtype", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _lib.muon_hparams_default.argtypes = [ctypes.POINTER(muon_hparams)]
 _lib.muon_hparams_default.restype = None
@@ -107,6 +118,11 @@ _lib.muon_tune_save.argtypes = [_P, ctypes.c_char_p]
 _lib.muon_tune_save.restype = ctypes.c_int
 _lib.muon_tune_load.argtypes = [_P, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int)]
 _lib.muon_tune_load.restype = ctypes.c_int
+_lib.muon_adamw_hparams_default.argtypes = [ctypes.POINTER(muon_adamw_hparams)]
+_lib.muon_adamw_hparams_default.restype = None
+_lib.muon_adamw_step.argtypes = [_P, ctypes.POINTER(muon_adamw_tensor), ctypes.c_int,
+                                 ctypes.POINTER(muon_adamw_hparams), _P]
+_lib.muon_adamw_step.restype = ctypes.c_int
 _lib.muon_destroy.argtypes = [_P]
 _lib.muon_destroy.restype = ctypes.c_int
 _lib.muon_status_str.argtypes = [ctypes.c_int]
@@ -240,6 +256,39 @@ def muon_tune_load(ctx, path: str) -> int:
     return n.value
 
 
+def make_adamw_hparams(**kw) -> muon_adamw_hparams:
+    """AdamW defaults from the library, with the given fields replaced (names as in muon.h;
+    w_dtype / g_dtype accept "f32" / "bf16")."""
+    hp = muon_adamw_hparams()
+    _lib.muon_adamw_hparams_default(ctypes.byref(hp))
+    for k, v in kw.items():
+        if k in ("w_dtype", "g_dtype"):
+            v = DTYPES.get(v, v)
+        setattr(hp, k, v)
+    return hp
+
+
+def adamw_tensor_list(tensors) -> ctypes.Array:
+    """Build a ``muon_adamw_tensor[]`` from (W, G, m, v) torch tensors (numel from W) or from
+    (W, G, m, v, numel) raw pointer tuples."""
+    arr = (muon_adamw_tensor * max(len(tensors), 1))()
+    for i, t in enumerate(tensors):
+        if len(t) == 5:
+            arr[i] = muon_adamw_tensor(t[0], t[1], t[2], t[3], int(t[4]))
+        else:
+            W, G, m, v = t
+            arr[i] = muon_adamw_tensor(W.data_ptr(), G.data_ptr(), m.data_ptr(), v.data_ptr(), W.numel())
+    return arr
+
+
+def muon_adamw_step(ctx, tensors, hp: muon_adamw_hparams, stream_ptr=None, count=None) -> int:
+    arr = tensors if isinstance(tensors, ctypes.Array) else adamw_tensor_list(tensors)
+    n = len(tensors) if count is None else count
+    if stream_ptr is None:
+        stream_ptr = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return _lib.muon_adamw_step(ctx, arr, n, ctypes.byref(hp), stream_ptr)
+
+
 def muon_destroy(ctx) -> int:
     return _lib.muon_destroy(ctx)
 
@@ -248,5 +297,6 @@ def exported_symbols() -> list:
     """Names of the C entry points this binding resolved (each must exist in the .so)."""
     return [n for n in ("muon_hparams_default", "muon_init", "muon_workspace_size", "muon_step",
                         "muon_plan_info", "muon_debug_gemm", "muon_profile_read", "muon_tune_save",
-                        "muon_tune_load", "muon_destroy", "muon_status_str")
+                        "muon_tune_load", "muon_adamw_hparams_default", "muon_adamw_step",
+                        "muon_destroy", "muon_status_str")
             if hasattr(_lib, n)]

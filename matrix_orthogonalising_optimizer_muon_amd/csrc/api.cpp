@@ -1067,6 +1067,74 @@ int muon_profile_read(muon_ctx* ctx, muon_profile_entry* out, int capacity, int*
   }
 }
 
+void muon_adamw_hparams_default(muon_adamw_hparams* hp) {
+  if (!hp) return;
+  hp->lr = 1e-3f;
+  hp->beta1 = 0.9f;
+  hp->beta2 = 0.999f;
+  hp->eps = 1e-8f;
+  hp->weight_decay = 0.01f;
+  hp->step = 1;
+  hp->w_dtype = MUON_F32;
+  hp->g_dtype = MUON_BF16;
+}
+
+int muon_adamw_step(muon_ctx* ctx, const muon_adamw_tensor* tensors, int count, const muon_adamw_hparams* hp,
+                    void* stream) {
+  try {
+    if (!ctx || !hp || count < 0 || (count > 0 && !tensors)) return MUON_ERR_ARG;
+    if (!finite(hp->lr) || !finite(hp->weight_decay) || !finite(hp->eps) || hp->eps < 0.0f) return MUON_ERR_ARG;
+    if (!finite(hp->beta1) || !finite(hp->beta2) || hp->beta1 < 0.0f || hp->beta1 >= 1.0f ||
+        hp->beta2 < 0.0f || hp->beta2 >= 1.0f || hp->step < 1)
+      return MUON_ERR_ARG;
+    if ((hp->w_dtype != MUON_F32 && hp->w_dtype != MUON_BF16) || (hp->g_dtype != MUON_F32 && hp->g_dtype != MUON_BF16))
+      return MUON_ERR_ARG;
+    for (int i = 0; i < count; ++i) {
+      const muon_adamw_tensor& t = tensors[i];
+      if (t.numel < 0) return MUON_ERR_ARG;
+      if (t.numel > 0 && (!t.W || !t.G || !t.m || !t.v)) return MUON_ERR_ARG;
+    }
+    if (count == 0) return MUON_OK;
+    if (ctx->device < 0) return MUON_ERR_DEVICE;
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return MUON_ERR_HIP;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    // bias corrections in double, then fp32 (as the kernel computes)
+    const double bc1 = 1.0 - std::pow(static_cast<double>(hp->beta1), hp->step);
+    const double bc2 = 1.0 - std::pow(static_cast<double>(hp->beta2), hp->step);
+    AdamChunk c;
+    std::memset(&c, 0, sizeof(c));
+    c.w_bf16 = hp->w_dtype == MUON_BF16; c.g_bf16 = hp->g_dtype == MUON_BF16;
+    c.lr = hp->lr; c.wd = hp->weight_decay; c.b1 = hp->beta1; c.b2 = hp->beta2; c.eps = hp->eps;
+    c.bc1 = static_cast<float>(bc1);
+    c.bc2s = static_cast<float>(std::sqrt(bc2));
+    int64_t blocks = 0;
+    auto flush = [&]() -> hipError_t {
+      const hipError_t e = launch_adamw(c, blocks, st);
+      c.n = 0;
+      blocks = 0;
+      return e;
+    };
+    for (int i = 0; i < count; ++i) {
+      const muon_adamw_tensor& t = tensors[i];
+      if (t.numel == 0) continue;
+      const int64_t nb = adam_blocks(t.numel);
+      if (c.n == kAdamChunk || blocks + nb > (int64_t{1} << 31) - 1) MUON_HIP(flush());
+      AdamTensor& a = c.t[c.n++];
+      a.W = t.W; a.G = t.G; a.m = t.m; a.v = t.v;
+      a.numel = t.numel;
+      a.block0 = blocks;
+      auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) % 16) == 0; };
+      a.vec = al16(t.W) && al16(t.G) && al16(t.m) && al16(t.v);
+      blocks += nb;
+    }
+    MUON_HIP(flush());
+    return MUON_OK;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
 int muon_destroy(muon_ctx* ctx) {
   if (!ctx) return MUON_OK;
   if (ctx->device >= 0) {

@@ -153,6 +153,30 @@ struct SmallParams {
 hipError_t launch_small_ns(const SmallParams& p, hipStream_t st);
 constexpr int kSmallMaxElems = 64 * 1024;  // padded m' n' the single-workgroup kernel takes
 
+// AdamW over up to kAdamChunk tensors per launch (descriptors travel in the kernel
+// arguments). Tensor i covers workgroups [block0, block0 + adam_blocks(numel)).
+constexpr int kAdamChunk = 24;
+struct AdamTensor {
+  void* W;
+  const void* G;
+  float* m;
+  float* v;
+  int64_t numel;
+  int64_t block0;
+  int32_t vec;      // all four arrays 16-byte aligned: 8-element vector accesses
+  int32_t pad_;
+};
+struct AdamChunk {
+  AdamTensor t[kAdamChunk];
+  int32_t n;
+  int32_t w_bf16, g_bf16;
+  float lr, wd, b1, b2, eps;
+  float bc1;        // 1 - beta1^t
+  float bc2s;       // sqrt(1 - beta2^t)
+};
+int64_t adam_blocks(int64_t numel);
+hipError_t launch_adamw(const AdamChunk& c, int64_t blocks, hipStream_t st);
+
 // Copy up to kTableChunk descriptors (passed by value) into device memory.
 constexpr int kTableChunk = 48;
 struct TableChunk {

@@ -50,7 +50,8 @@ def test_struct_layouts_match_c_compiler(tmp_path):
     """Field offsets and sizes of the header's structs, as gcc lays them out, equal the
     ctypes mirrors the binding uses."""
     structs = {"muon_matrix": B.muon_matrix, "muon_hparams": B.muon_hparams,
-               "muon_plan_entry": B.muon_plan_entry, "muon_profile_entry": B.muon_profile_entry}
+               "muon_plan_entry": B.muon_plan_entry, "muon_profile_entry": B.muon_profile_entry,
+               "muon_adamw_tensor": B.muon_adamw_tensor, "muon_adamw_hparams": B.muon_adamw_hparams}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
     for name, cls in structs.items():
         lines.append(f'printf("{name} size %zu\\n", sizeof({name}));')
@@ -345,3 +346,28 @@ def test_auto_schedule_examples(hctx):
         assert tuple(e[0].segments[:e[0].n_segments]) == (12,)
     finally:
         B.muon_destroy(mctx)
+
+
+# ---------------------------------------------------------------- AdamW companion
+
+def test_adamw_defaults_and_validation(hctx):
+    hp = B.make_adamw_hparams()
+    assert (hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step) == pytest.approx(
+        (1e-3, 0.9, 0.999, 1e-8, 0.01, 1))
+    assert (hp.w_dtype, hp.g_dtype) == (B.MUON_F32, B.MUON_BF16)
+    P = FAKE
+    good = [(P, P, P, P, 1000), (0, 0, 0, 0, 0)]           # an empty tensor may hold nulls
+    f = B._lib.muon_adamw_step
+    arr = B.adamw_tensor_list(good)
+    assert f(hctx, arr, 2, ctypes.byref(hp), None) == B.MUON_ERR_DEVICE   # valid; host-only ctx
+    assert f(hctx, arr, 0, ctypes.byref(hp), None) == B.MUON_OK
+    assert f(None, arr, 2, ctypes.byref(hp), None) == B.MUON_ERR_ARG
+    assert f(hctx, None, 2, ctypes.byref(hp), None) == B.MUON_ERR_ARG
+    assert f(hctx, arr, -1, ctypes.byref(hp), None) == B.MUON_ERR_ARG
+    assert f(hctx, arr, 2, None, None) == B.MUON_ERR_ARG
+    for bad in [[(P, P, P, P, -1)], [(P, 0, P, P, 10)], [(P, P, P, 0, 10)], [(0, P, P, P, 10)]]:
+        assert f(hctx, B.adamw_tensor_list(bad), 1, ctypes.byref(hp), None) == B.MUON_ERR_ARG, bad
+    for kw in [dict(beta1=1.0), dict(beta2=-0.1), dict(eps=-1e-8), dict(lr=float("nan")), dict(step=0),
+               dict(weight_decay=float("inf")), dict(w_dtype=3), dict(g_dtype=-1)]:
+        assert f(hctx, arr, 2, ctypes.byref(B.make_adamw_hparams(**kw)), None) == B.MUON_ERR_ARG, kw
+

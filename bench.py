@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--mode", default="auto", choices=["auto", "gram", "plain", "auto_schedule"],
                     help="NS form: auto (plain or Gram 2+2+1 per shape, the default), gram, plain, or "
                          "auto_schedule (plain or Gram with the cheapest segment count per shape)")
+    ap.add_argument("--adamw", action="store_true",
+                    help="also time the AdamW step over the 7B shape set's non-matrix parameters "
+                         "(embedding, head, biases, norms; fp32 W / m / v, bf16 G)")
     ap.add_argument("--tune-cache", default=None,
                     help="tile-choice file: loaded before the warmup when it exists, written after "
                          "it (so that separate profiling runs use the same kernels)")
@@ -134,6 +137,40 @@ def traffic_record(workload):
     if rec.get("source_sha256") != h.hexdigest():
         return None
     return rec
+
+
+def adamw_bench(B, ctx, torch, args):
+    """muon_adamw_step over the non-matrix parameters of the 7B shape set, inputs resident
+    in HBM; algorithmic bytes 26 per element (W and m, v fp32 read + written, G bf16 read)."""
+    from matrix_orthogonalising_optimizer_muon_amd import workloads as wl
+    sizes = [n for _, n in wl.ADAMW_SETS["dense_7b_nonmatrix"]]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    ts = []
+    for n in sizes:
+        W = 0.02 * torch.randn(n, generator=gen, device="cuda")
+        G = (1e-3 * torch.randn(n, generator=gen, device="cuda")).to(torch.bfloat16)
+        ts.append((W, G, torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")))
+    arr = B.adamw_tensor_list(ts)
+    stream = torch.cuda.current_stream()
+    elems = sum(sizes)
+    for t in range(1, args.warmup + 1):
+        B.check(B.muon_adamw_step(ctx, arr, B.make_adamw_hparams(step=t), stream.cuda_stream, len(ts)), "adamw")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for t in range(args.steps):
+        B.check(B.muon_adamw_step(ctx, arr, B.make_adamw_hparams(step=args.warmup + 1 + t), stream.cuda_stream,
+                                  len(ts)), "adamw")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = 26.0 * elems / (ms * 1e-3) / 1e9
+    print(f"[bench] adamw companion: {len(ts)} tensors, {elems / 1e6:.1f} M elements, {ms:.3f} ms/step, "
+          f"{gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    return {"set": "dense_7b_nonmatrix", "tensors": len(ts), "elements": elems, "ms_per_step": round(ms, 4),
+            "bytes_per_element": 26, "achieved_gbs": round(gbs, 1), "peak_gbs": HBM_PEAK_GBS,
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -279,6 +316,8 @@ def main():
         out["roofline"]["traffic_kernel"] = st["kernel"]
         if "trace_avg_us" in st:
             out["roofline"]["rocprof_avg_us"] = st["trace_avg_us"]
+    if args.adamw:
+        out["adamw_companion"] = adamw_bench(B, ctx, torch, args)
     B.muon_destroy(ctx)
     B.muon_destroy(pctx)
     print(json.dumps(out), flush=True)

@@ -103,6 +103,19 @@ WORKLOADS = {
 }
 
 
+# Parameters of the 7B decoder shape set that stay with AdamW (MuonX article, section 2:
+# embeddings, biases and similar parameters): token embedding and output head
+# (vocabulary 152064 x hidden 3584, the untied head of the Qwen2.5-7B shape set), the
+# q / k / v biases of 28 layers (3584, 512, 512) and 57 norm weights of 3584.
+ADAMW_SETS = {
+    "dense_7b_nonmatrix": (
+        [("embed", 152064 * 3584), ("lm_head", 152064 * 3584)]
+        + [(f"L{l}.{b}", n) for l in range(28) for b, n in (("q_bias", 3584), ("k_bias", 512), ("v_bias", 512))]
+        + [(f"norm{i}", 3584) for i in range(57)]
+    ),
+}
+
+
 def rng_for(w: Workload, step: int, index: int, role: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.wid, step, index, role])))
 

@@ -46,3 +46,117 @@ class MuonUpdate:
             self.close()
         except Exception:
             pass
+
+
+def _dtype_name(dt: torch.dtype) -> str:
+    if dt == torch.float32:
+        return "f32"
+    if dt == torch.bfloat16:
+        return "bf16"
+    raise TypeError(f"parameters must be float32 or bfloat16, got {dt}")
+
+
+class MuonWithAdamW(torch.optim.Optimizer):
+    """torch.optim-style optimizer over a model's parameters: 2-D hidden weights go to the
+    Muon update (``muon_step``), everything else -- embeddings, output heads, biases, norm
+    weights -- to AdamW (``muon_adamw_step``), as the MuonX article (section 2) describes
+    practice; integration is the announcement's "replace the optimizer".
+
+    ``params``: an iterable of parameters or of ``(name, parameter)`` pairs. A 2-D parameter
+    goes to AdamW when its name contains one of ``adamw_names``. All state (Muon momentum,
+    AdamW moments, the Muon workspace) lives on the parameters' device; ``step()`` launches
+    one ``muon_step`` per (weight dtype, gradient dtype) group and one ``muon_adamw_step``
+    on the current stream, with no host synchronisation. Parameters without a gradient are
+    skipped for that step.
+    """
+
+    def __init__(self, params, *, lr: float = 0.02, momentum: float = 0.95, weight_decay: float = 0.0,
+                 nesterov: bool = True, segments=(2, 2, 1), mode: str = "auto", ns_dtype: str = "bf16",
+                 momentum_dtype: str = "bf16", adamw_lr: float = 3e-4, adamw_betas=(0.9, 0.95),
+                 adamw_eps: float = 1e-8, adamw_weight_decay: float = 0.0,
+                 adamw_names=("embed", "lm_head", "wte", "wpe", "head")):
+        named = []
+        for i, p in enumerate(params):
+            named.append(p if isinstance(p, tuple) else (f"param{i}", p))
+        muon, adamw = [], []
+        for name, p in named:
+            if not p.requires_grad:
+                continue
+            if p.ndim == 2 and not any(k in name for k in adamw_names):
+                muon.append(p)
+            else:
+                adamw.append(p)
+        defaults = dict(lr=lr, adamw_lr=adamw_lr)
+        super().__init__([{"params": muon, "kind": "muon"}, {"params": adamw, "kind": "adamw"}], defaults)
+        self._muon_hp = dict(lr=lr, momentum=momentum, weight_decay=weight_decay, nesterov=nesterov,
+                             segments=segments, mode=mode, ns_dtype=ns_dtype)
+        self._adamw_hp = dict(lr=adamw_lr, beta1=adamw_betas[0], beta2=adamw_betas[1], eps=adamw_eps,
+                              weight_decay=adamw_weight_decay)
+        self._momentum_dtype = {"bf16": torch.bfloat16, "f32": torch.float32}[momentum_dtype]
+        self._mdt = momentum_dtype
+        dev = (muon + adamw)[0].device if (muon or adamw) else torch.device("cuda")
+        self._ctx = B.muon_init(dev.index if dev.index is not None else torch.cuda.current_device())
+        self._adamw_step = 0
+        self._ws = None
+        self._ws_bytes = 0
+        for p in muon:
+            self.state[p]["M"] = torch.zeros_like(p, dtype=self._momentum_dtype)
+        for p in adamw:
+            self.state[p]["m"] = torch.zeros_like(p, dtype=torch.float32)
+            self.state[p]["v"] = torch.zeros_like(p, dtype=torch.float32)
+
+    def _workspace(self, nbytes: int, device) -> int:
+        if self._ws is None or self._ws_bytes < nbytes:
+            self._ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+            self._ws_bytes = nbytes
+        return self._ws.data_ptr()
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        stream = torch.cuda.current_stream().cuda_stream
+        muon_group, adamw_group = self.param_groups
+        # Muon: one call per (weight dtype, gradient dtype); the lr may be changed per step
+        # through the group's "lr" entry, like torch schedulers do.
+        by_dtype = {}
+        for p in muon_group["params"]:
+            if p.grad is None:
+                continue
+            by_dtype.setdefault((_dtype_name(p.dtype), _dtype_name(p.grad.dtype)), []).append(p)
+        for (wd, gd), ps in by_dtype.items():
+            hp = B.make_hparams(**{**self._muon_hp, "lr": muon_group["lr"]}, w_dtype=wd, g_dtype=gd,
+                                m_dtype=self._mdt)
+            mats = [(p, p.grad, self.state[p]["M"]) for p in ps]
+            nbytes = B.muon_workspace_size(self._ctx, mats, hp)
+            ws = self._workspace(nbytes, ps[0].device)
+            B.check(B.muon_step(self._ctx, mats, hp, ws, nbytes, stream), "muon_step")
+        # AdamW: one call per (weight dtype, gradient dtype), all tensors of it together.
+        self._adamw_step += 1
+        by_dtype = {}
+        for p in adamw_group["params"]:
+            if p.grad is None:
+                continue
+            by_dtype.setdefault((_dtype_name(p.dtype), _dtype_name(p.grad.dtype)), []).append(p)
+        for (wd, gd), ps in by_dtype.items():
+            hp = B.make_adamw_hparams(**{**self._adamw_hp, "lr": adamw_group.get("adamw_lr", self._adamw_hp["lr"])},
+                                      step=self._adamw_step, w_dtype=wd, g_dtype=gd)
+            ts = [(p, p.grad, self.state[p]["m"], self.state[p]["v"]) for p in ps]
+            B.check(B.muon_adamw_step(self._ctx, ts, hp, stream), "muon_adamw_step")
+        return loss
+
+    def muon_parameters(self):
+        return list(self.param_groups[0]["params"])
+
+    def adamw_parameters(self):
+        return list(self.param_groups[1]["params"])
+
+    def __del__(self):
+        try:
+            if getattr(self, "_ctx", None) is not None:
+                B.muon_destroy(self._ctx)
+                self._ctx = None
+        except Exception:
+            pass

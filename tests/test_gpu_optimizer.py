@@ -1,0 +1,77 @@
+"""The drop-in optimizer (MuonWithAdamW) on a small model: 2-D hidden weights follow the
+Muon oracle, embeddings / head / biases / norm weights the AdamW oracle, over two steps of
+real backward passes (gradients from torch autograd on the GPU, copied to the host as
+oracle inputs)."""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from oracle import adamw as oa  # noqa: E402
+from oracle import flop_model  # noqa: E402
+from oracle import muon as om  # noqa: E402
+
+
+class Tiny(torch.nn.Module):
+    def __init__(self):
+        super().__init__()
+        self.embed = torch.nn.Embedding(97, 64)
+        self.up = torch.nn.Linear(64, 320)
+        self.down = torch.nn.Linear(320, 64, bias=False)
+        self.norm = torch.nn.LayerNorm(64)
+        self.lm_head = torch.nn.Linear(64, 97, bias=False)
+
+    def forward(self, idx):
+        h = self.embed(idx)
+        h = h + self.down(torch.relu(self.up(h)))
+        return self.lm_head(self.norm(h))
+
+
+def rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def test_muon_with_adamw_two_steps():
+    from matrix_orthogonalising_optimizer_muon_amd.optimizer import MuonWithAdamW
+    torch.manual_seed(0)
+    model = Tiny().cuda()
+    names = dict((id(p), n) for n, p in model.named_parameters())
+    opt = MuonWithAdamW(model.named_parameters(), lr=0.02, momentum=0.95, adamw_lr=1e-3,
+                        adamw_betas=(0.9, 0.95), adamw_weight_decay=0.1)
+    muon_names = sorted(names[id(p)] for p in opt.muon_parameters())
+    assert muon_names == ["down.weight", "up.weight"]
+    assert sorted(names[id(p)] for p in opt.adamw_parameters()) == sorted(
+        ["embed.weight", "up.bias", "norm.weight", "norm.bias", "lm_head.weight"])
+
+    ref = {n: p.detach().double().cpu().numpy() for n, p in model.named_parameters()}
+    mom = {n: np.zeros_like(v) for n, v in ref.items()}
+    m1 = {n: np.zeros_like(v) for n, v in ref.items()}
+    v1 = {n: np.zeros_like(v) for n, v in ref.items()}
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    for t in (1, 2):
+        idx = torch.randint(0, 97, (8, 16), device="cuda", generator=gen)
+        loss = torch.nn.functional.cross_entropy(model(idx).reshape(-1, 97), idx.reshape(-1))
+        opt.zero_grad(set_to_none=True)
+        loss.backward()
+        grads = {n: p.grad.detach().double().cpu().numpy() for n, p in model.named_parameters()}
+        before = {n: p.detach().double().cpu().numpy() for n, p in model.named_parameters()}
+        opt.step()
+        torch.cuda.synchronize()
+        for n, p in model.named_parameters():
+            got = p.detach().double().cpu().numpy()
+            if n in muon_names:
+                r, c = ref[n].shape
+                mode = "gram" if flop_model.dense_flops(r, c, "gram") < flop_model.dense_flops(r, c, "plain") \
+                    else "plain"
+                W_new, M_new, O = om.muon_step(ref[n], grads[n], mom[n], lr=0.02, mu=0.95, wd=0.0, mode=mode)
+                assert rel((before[n] - got) / 0.02, O) <= 2e-2, (n, t)
+                ref[n], mom[n] = W_new, M_new
+            else:
+                W_new, m1[n], v1[n] = oa.adamw_step(ref[n], grads[n], m1[n], v1[n], t, lr=1e-3, beta1=0.9,
+                                                    beta2=0.95, eps=1e-8, wd=0.1)
+                # fp32 kernel vs fp64 oracle on an fp64 trajectory (fp32-stored W): tiny drift
+                assert np.allclose(got, W_new, rtol=1e-5, atol=1e-7), (n, t)
+                ref[n] = W_new
+

@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--mode", default="auto", choices=["auto", "gram", "plain", "auto_schedule"],
                     help="NS form: auto (plain or Gram 2+2+1 per shape, the default), gram, plain, or "
                          "auto_schedule (plain or Gram with the cheapest segment count per shape)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one muon_step captured in a HIP graph (after the warm-up "
+                         "has measured the tiles) instead of eager calls")
     ap.add_argument("--adamw", action="store_true",
                     help="also time the AdamW step over the 7B shape set's non-matrix parameters "
                          "(embedding, head, biases, norms; fp32 W / m / v, bf16 G)")
@@ -225,13 +228,30 @@ def main():
     print(f"[bench] warmup done ({args.warmup} steps), workspace {nbytes / 2**30:.2f} GiB",
           file=sys.stderr, flush=True)
 
+    graph = None
+    if args.graph:
+        # one step captured on a side stream; replays run on the launch stream
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                B.check(B.muon_step(ctx, arr, hp, ws.data_ptr(), nbytes, side.cuda_stream, count=len(mats)),
+                        "muon_step (capture)")
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+
     # Timed region: exactly K steps between two events on the launch stream.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
-        step(ctx)
+        if graph is not None:
+            graph.replay()
+        else:
+            step(ctx)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -279,6 +299,7 @@ def main():
         "dtype": "bf16" if w.ns_dtype == "bf16" else "f32",
         "data": f"synthetic ({data})",
         "config": {"workload": w.name, "matrices": len(w.matrices), "elements": w.elements,
+                   "launch": "hip graph replay" if args.graph else "eager",
                    "shapes": sorted({f"{s.rows}x{s.cols}" for s in w.matrices}),
                    "ns": {"auto": "auto (FLOP-model dispatch: Gram 2+2+1 or plain 5 rounds)",
                           "gram": "Gram 2+2+1", "plain": "plain 5 rounds",

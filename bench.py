@@ -246,16 +246,24 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    # One event between consecutive steps as well (recording adds no synchronisation), for
+    # the per-step distribution.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps - 1)]
     e0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
             step(ctx)
+        if i < args.steps - 1:
+            marks[i].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+    edges = [e0] + marks + [e1]
+    per_step = sorted(edges[i].elapsed_time(edges[i + 1]) for i in range(args.steps))
+    pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
           file=sys.stderr, flush=True)
 
@@ -293,6 +301,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,

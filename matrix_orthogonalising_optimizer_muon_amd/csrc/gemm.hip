@@ -23,9 +23,6 @@
 
 #include "internal.hpp"
 
-#ifndef MUON_SCHED_GROUPS
-#define MUON_SCHED_GROUPS 1
-#endif
 
 namespace muon {
 namespace {
@@ -322,15 +319,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// The same, and every LDS access of this wave returned (lgkmcnt 0).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 
 // Same product as gemm_kernel, with operands moved global -> LDS by the CDNA4 direct
 // loads (16 bytes per lane, lane l writing LDS bytes [16 l, 16 l + 16) of the
 // instruction's 1 KB window = 64 / CH rows of CH 16-byte chunks). The XOR swizzle moves
 // to the global side: lane l of a window loads logical chunk (l % CH) ^ f(row). NS LDS
-// stages form a ring; slice k + NS - 1 is issued before slice k is computed, so NS - 1
-// slices of loads are in flight and no staging registers are needed. A slice is CH
-// chunks of K per row: CH = 4 halves the slice, so twice as many stages fit in the same
-// LDS and more load latency is covered.
+// stages form a ring; while slice k is computed, slices k + 1 .. k + NS - 1 are in flight
+// or landed, so no staging registers are needed. A slice is CH chunks of K per row:
+// CH = 4 halves the slice, so twice as many stages fit in the same LDS and more load
+// latency is covered. With KS = 2 the two k-groups of waves take alternate k-steps of
+// every slice and add their partial sums through LDS at the end.
 template <int KIND, int BM, int BN, int WM, int WN, int NS, int KS, int CH, bool SYM, int EPI, int TAG>
 __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmParams p) {
   using TO = typename OutT<KIND>::T;
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   constexpr int KL = KSTEPS / KS;                          // k-steps per wave per slice
   constexpr int D = NS - 1;                                // slices in flight
   static_assert(NS >= 2 && (KS == 1 || KS == 2), "stages / k-groups");
-  static_assert(KS == 1 || BM * BN * 4 <= NS * STAGE * 16, "k-group reduction fits in LDS");
+  static_assert(KS == 1 || (KS / 2) * BM * BN * 4 <= NS * STAGE * 16, "k-group reduction fits in LDS");
 
   __shared__ u32x4 lds[NS * STAGE];
 
@@ -422,58 +426,127 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   };
 
   // Prologue: slices 0 .. D-1 (clamped: past the end the last slice is reloaded into a
-  // stage that is never read, so every iteration issues the same number of loads).
+  // stage that is never read, so every slice issues the same number of loads), then slice
+  // 0 is awaited, slice D goes to the one stage still unused and the first k-step's
+  // fragments are read.
 #pragma unroll
   for (int s0 = 0; s0 < D; ++s0) issue(s0, min(s0, nk - 1) * BK);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<(D - 1) * (IA + IB)>();  // this wave's part of slice kt has landed
-    __builtin_amdgcn_s_barrier();         // ... and every wave's; slice kt-1's stage is free
-    issue((kt + D) % NS, min(kt + D, nk - 1) * BK);
+  wait_vmcnt<(D - 1) * (IA + IB)>();
+  __builtin_amdgcn_s_barrier();
+  issue(D, min(D, nk - 1) * BK);
+  load_frags(0, lds, lds + BM * CH, kk0);
+
+  // One slice: the MFMAs of every k-step run while the fragments of the next k-step are
+  // read. Before the last k-step's MFMAs the workgroup synchronises once: this wave's
+  // reads of the slice have returned (lgkmcnt 0) and its loads of the next slice have
+  // landed; after the barrier the slice's stage is free for the loads of slice kt + NS
+  // and the next slice's first fragments are read. So LDS read latency always hides
+  // behind MFMAs. P is the fragment buffer of the slice's first k-step.
+  auto slice = [&](int kt, auto par_tag, auto next_tag) {
+    constexpr int P = decltype(par_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;  // a slice follows (all but the last)
+    constexpr int NMF = (KIND == KIND_F32 ? 4 : 1) * FM * FN;  // MFMA instructions per k-step
     const u32x4* la = lds + (kt % NS) * STAGE;
     const u32x4* lb = la + BM * CH;
-    load_frags(0, la, lb, kk0);
 #pragma unroll
     for (int kl = 0; kl < KL; ++kl) {
-      if (kl + 1 < KL) load_frags((kl + 1) & 1, la, lb, kk0 + kl + 1);
+      const int cur = (P + kl) & 1;
+      if (kl + 1 < KL) {
+        load_frags(cur ^ 1, la, lb, kk0 + kl + 1);
+      } else if constexpr (NEXT) {
+        // Before the barrier: M0(first MFMA) R1 M0(rest) R2 M1 ... for the k-steps before
+        // the last one, then nothing may move across.
+#pragma unroll
+        for (int kk = 0; kk + 1 < KL; ++kk) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NMF - 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt_lgkm0<(D - 1) * (IA + IB)>();
+        __builtin_amdgcn_s_barrier();
+        issue(kt % NS, min(kt + NS, nk - 1) * BK);
+        const u32x4* na = lds + ((kt + 1) % NS) * STAGE;
+        load_frags(cur ^ 1, na, na + BM * CH, kk0);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) mma<KIND>(acc[i][j], fa[kl & 1][i], fb[kl & 1][j]);
+        for (int j = 0; j < FN; ++j) mma<KIND>(acc[i][j], fa[cur][i], fb[cur][j]);
     }
-#if MUON_SCHED_GROUPS
-    // Order the slice as R0 R1 M0 R2 M1 ... (Rk: LDS fragment reads of k-step k, Mk: its
-    // MFMAs), so each k-step's reads are in flight during the previous MFMAs.
-    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-#pragma unroll
-    for (int kl = 1; kl < KL; ++kl) {
+    // After the barrier: the next slice's first fragment reads, then the last k-step's
+    // MFMAs (the last slice: the same pattern as before the barrier, without the reads of a
+    // next slice). The first MFMA of a k-step goes ahead of the reads because its
+    // fragments may still be in flight and the compiler waits for every read issued
+    // before it.
+    if constexpr (NEXT) {
       __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, (KIND == KIND_F32 ? 4 : 1) * FM * FN, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk + 1 < KL; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, (KIND == KIND_F32 ? 4 : 1) * FM * FN, 0);
-#endif
+  };
+  // The last slice is peeled off, so the steady-state loop has no branch around its
+  // barrier (a control-flow join there makes the compiler wait for every LDS read,
+  // including the next slice's, before the last k-step's MFMAs).
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using YES = std::true_type;
+  using NO = std::false_type;
+  if constexpr (KL % 2 == 0) {
+    for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, I0{}, YES{});
+    slice(nk - 1, I0{}, NO{});
+  } else {
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+      slice(kt, I0{}, YES{});
+      slice(kt + 1, I1{}, YES{});
+    }
+    if (kt + 2 == nk) {
+      slice(kt, I0{}, YES{});
+      slice(kt + 1, I1{}, NO{});
+    } else {
+      slice(kt, I0{}, NO{});
+    }
   }
   wait_vmcnt<0>();
 
-  if constexpr (KS == 2) {
-    // The second k-group hands its partial sums to the first through LDS.
+  if constexpr (KS > 1) {
+    // Tree reduction of the k-groups' partial sums through LDS: in each round the upper
+    // half of the remaining k-groups writes its partials, the lower half adds them
+    // ((g0 + g2) + (g1 + g3) for four groups: a fixed order).
     float* red = reinterpret_cast<float*>(lds);
-    __syncthreads();
-    if (kgrp == 1) {
+    constexpr int REG = BM * BN;  // floats per k-group partial
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int half = KS / 2; half >= 1; half /= 2) {
+      __syncthreads();
+      if (kgrp >= half && kgrp < 2 * half) {
+        float* r = red + (kgrp - half) * REG;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) red[((i * FN + j) * 16 + e) * (64 * NWC) + wloc * 64 + lane] = acc[i][j][e];
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r[((i * FN + j) * 16 + e) * (64 * NWC) + wloc * 64 + lane] = acc[i][j][e];
+      }
+      __syncthreads();
+      if (kgrp < half) {
+        const float* r = red + kgrp * REG;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] += r[((i * FN + j) * 16 + e) * (64 * NWC) + wloc * 64 + lane];
+      }
     }
-    __syncthreads();
-    if (kgrp == 1) return;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] += red[((i * FN + j) * 16 + e) * (64 * NWC) + wloc * 64 + lane];
+    if (kgrp != 0) return;
   }
 
   epilogue<KIND, BM, BN, WM, WN, SYM, EPI, FM, FN, TO>(p, acc, mat, tm, tn, m0, n0, wm0, wn0, lane);

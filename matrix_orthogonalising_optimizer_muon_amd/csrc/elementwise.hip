@@ -172,8 +172,20 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const float* partial
   __shared__ double red[256];
   const int mat = blockIdx.x;
   const float* src = partials + static_cast<int64_t>(mat) * per_matrix;
+  // Partials i = tid, tid + 256, ... are added in that order; their loads are issued
+  // eight at a time (the partials come from every XCD's workgroups, so each load goes
+  // past this XCD's L2), and the zero padding past the end leaves the sum unchanged.
   double acc = 0.0;
-  for (int i = threadIdx.x; i < per_matrix; i += 256) acc += static_cast<double>(src[i]);
+  for (int base = threadIdx.x; base < per_matrix; base += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * 256;
+      v[u] = i < per_matrix ? src[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += static_cast<double>(v[u]);
+  }
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {

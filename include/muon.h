@@ -90,7 +90,9 @@ typedef struct muon_matrix {
  *                       rounds on the bf16 path). A Gram segment count k costs k SYRK and k
  *                       apply products plus 4R - 3k m'xm' products, plain NS R of each; the
  *                       costs are the measured times of the shape's stages once a step has
- *                       measured its tiles, else the FLOP counts the kernels perform.
+ *                       measured its tiles, else the FLOP counts the kernels perform. The
+ *                       choice may change once the tiles are measured; the workspace size
+ *                       covers the Gram form for every shape, so it does not change.
  *   w_dtype:            MUON_F32 or MUON_BF16
  *   g_dtype, m_dtype:   MUON_F32 or MUON_BF16
  *   ns_dtype:           MUON_BF16: bf16 iterate with fp32-accumulate MFMA, the m'xm'

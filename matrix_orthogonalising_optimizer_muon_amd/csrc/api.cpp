@@ -259,7 +259,10 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
       off = align_up(off + ex * static_cast<size_t>(g.stride_x) * cnt);
     }
     g.stride_sq = g.Mp * g.Mp;
-    const int nsq = (g.mode == MUON_NS_GRAM) ? 4 : 2;
+    // The automatic schedule may pick plain NS before a shape's tiles are measured and
+    // Gram NS after, so it always reserves the Gram path's four m' x m' buffers: the
+    // workspace size does not change between steps.
+    const int nsq = (g.mode == MUON_NS_GRAM || hp.mode == MUON_NS_AUTO_SCHEDULE) ? 4 : 2;
     for (int k = 0; k < nsq; ++k) {
       g.off_sq[k] = off;
       off = align_up(off + esq * static_cast<size_t>(g.stride_sq) * cnt);

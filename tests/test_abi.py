@@ -371,3 +371,23 @@ def test_adamw_defaults_and_validation(hctx):
                dict(weight_decay=float("inf")), dict(w_dtype=3), dict(g_dtype=-1)]:
         assert f(hctx, arr, 2, ctypes.byref(B.make_adamw_hparams(**kw)), None) == B.MUON_ERR_ARG, kw
 
+
+
+def test_auto_schedule_workspace_covers_both_forms(hctx):
+    """The automatic schedule may run plain NS before a shape's tiles are measured and Gram
+    NS after: its workspace holds the Gram path's buffers whatever the plan, so a size
+    taken once stays valid for every later step."""
+    shapes = [(2048, 2048), (2560, 9728), (64, 256)]
+    mats = [(0, 0, 0, r, c) for r, c in shapes]
+    auto = B.muon_workspace_size(hctx, mats, B.make_hparams(mode="auto_schedule"))
+    gram = B.muon_workspace_size(hctx, mats, B.make_hparams(mode="gram"))
+    plain = B.muon_workspace_size(hctx, mats, B.make_hparams(mode="plain"))
+    assert auto == gram > plain
+    mctx = B.muon_init(-1, B.MUON_FLAG_MODEL_ONLY)
+    try:
+        e = plan(mctx, [(2048, 2048)], mode="auto_schedule")
+        assert e[0].mode == B.MUON_NS_PLAIN            # plain for this shape, Gram-sized anyway
+        assert B.muon_workspace_size(mctx, [(0, 0, 0, 2048, 2048)], B.make_hparams(mode="auto_schedule")) == \
+            B.muon_workspace_size(mctx, [(0, 0, 0, 2048, 2048)], B.make_hparams(mode="gram"))
+    finally:
+        B.muon_destroy(mctx)

@@ -160,6 +160,31 @@ def test_bf16_auto_schedule(B, ctx):
         assert sum(e.segments[:e.n_segments]) == 5
 
 
+def test_auto_schedule_fixed_workspace(B):
+    """A workspace sized once, before the first step measures any tile, serves every later
+    step of the automatic schedule (whose plan may switch between plain and Gram NS once
+    the stage times are measured), and the size it reports does not change."""
+    c = B.muon_init(0)
+    try:
+        shapes = [(1984, 1984), (1472, 1472), (704, 2880), (2880, 704)]
+        w = wl.custom("autows", shapes, structure="lowrank", rank=16, wid=217, steps=3)
+        st = GpuState(w)
+        hp = B.make_hparams(mode="auto_schedule")
+        st.load_gradients(0)
+        nbytes = B.muon_workspace_size(c, st.triples(), hp)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        for s in range(3):
+            st.load_gradients(s)
+            rc = B.muon_step(c, st.triples(), hp, ws.data_ptr(), nbytes)
+            torch.cuda.synchronize()
+            assert rc == B.MUON_OK, (s, B.muon_status_str(rc))
+            assert B.muon_workspace_size(c, st.triples(), hp) == nbytes
+        for x in st.W:
+            assert torch.isfinite(x).all()
+    finally:
+        B.muon_destroy(c)
+
+
 @pytest.mark.parametrize("segments", [(3, 2), (2, 3)])
 def test_bf16_2560x9728_long_segments(B, ctx, segments):
     """The single long matrix with two Gram segments of 3 and 2 rounds (the schedule the
@@ -169,14 +194,15 @@ def test_bf16_2560x9728_long_segments(B, ctx, segments):
 
 
 @pytest.mark.parametrize("mode", ["gram", "plain"])
-def test_bf16_split_k(B, ctx, mode):
-    """Single mid-size matrices: too few tiles for the GPU, so the symmetric stages split K
-    over several workgroups (last-arriver reduction)."""
+def test_bf16_few_tiles(B, ctx, mode):
+    """Single mid-size matrices with long K: fewer output tiles than the GPU has CUs, one
+    of them tall (transposed)."""
     w = wl.custom("splitk", [(512, 4096), (2048, 384)], structure="lowrank", rank=16, wid=210)
     check_step(B, ctx, w, mode=mode)
 
 
-def test_fp32_split_k(B, ctx):
+def test_fp32_few_tiles(B, ctx):
+    """The same on the fp32 path."""
     w = wl.custom("splitk32", [(256, 4096)], dtype="f32", wid=211)
     check_step(B, ctx, w, mode="gram")
     check_step(B, ctx, w, mode="plain")

@@ -4,8 +4,11 @@ workspace tensor, so one Muon update of every registered 2-D weight is one call.
 The DMuon announcement (agentren.cn, "three lines of code") and the MuonX article
 (section 3.3) describe integration as: name the participating matrices, replace the
 optimizer. Here: build ``MuonUpdate([(W, G, M), ...])`` once, call ``step()`` after
-each backward. Only 2-D hidden weights belong here (MuonX section 2: embeddings and
-biases stay on AdamW).
+each backward. The library keeps the tensors' addresses from construction on, so W, G
+and M must stay the same tensors (G a persistent gradient buffer that each backward
+fills, not a new ``.grad`` per step); ``MuonWithAdamW`` below takes the current ``.grad``
+at every step instead. Only 2-D hidden weights belong here (MuonX section 2: embeddings
+and biases stay on AdamW).
 """
 
 from __future__ import annotations
@@ -63,11 +66,17 @@ class MuonWithAdamW(torch.optim.Optimizer):
     practice; integration is the announcement's "replace the optimizer".
 
     ``params``: an iterable of parameters or of ``(name, parameter)`` pairs. A 2-D parameter
-    goes to AdamW when its name contains one of ``adamw_names``. All state (Muon momentum,
-    AdamW moments, the Muon workspace) lives on the parameters' device; ``step()`` launches
-    one ``muon_step`` per (weight dtype, gradient dtype) group and one ``muon_adamw_step``
+    goes to AdamW when its name contains one of ``adamw_names``. All parameters must be on
+    one GPU. All state (Muon momentum, AdamW moments and step counts, the Muon workspace)
+    lives on that device; ``step()`` launches one ``muon_step`` per (weight dtype, gradient
+    dtype) group and one ``muon_adamw_step`` per (weight dtype, gradient dtype, step count)
     on the current stream, with no host synchronisation. Parameters without a gradient are
-    skipped for that step.
+    skipped for that step (an AdamW parameter's step count then does not advance, so its
+    bias correction follows the steps it took part in).
+
+    The two parameter groups carry their own ``"lr"`` (``lr`` for Muon, ``adamw_lr`` for
+    AdamW), which ``step()`` reads every time, so ``torch.optim.lr_scheduler`` schedules
+    both.
     """
 
     def __init__(self, params, *, lr: float = 0.02, momentum: float = 0.95, weight_decay: float = 0.0,
@@ -86,8 +95,12 @@ class MuonWithAdamW(torch.optim.Optimizer):
                 muon.append(p)
             else:
                 adamw.append(p)
-        defaults = dict(lr=lr, adamw_lr=adamw_lr)
-        super().__init__([{"params": muon, "kind": "muon"}, {"params": adamw, "kind": "adamw"}], defaults)
+        defaults = dict(lr=lr)
+        super().__init__([{"params": muon, "kind": "muon", "lr": lr},
+                          {"params": adamw, "kind": "adamw", "lr": adamw_lr}], defaults)
+        devices = {p.device for p in muon + adamw}
+        if len(devices) > 1:
+            raise ValueError(f"all parameters must be on one device, got {sorted(map(str, devices))}")
         self._muon_hp = dict(lr=lr, momentum=momentum, weight_decay=weight_decay, nesterov=nesterov,
                              segments=segments, mode=mode, ns_dtype=ns_dtype)
         self._adamw_hp = dict(lr=adamw_lr, beta1=adamw_betas[0], beta2=adamw_betas[1], eps=adamw_eps,
@@ -96,7 +109,6 @@ class MuonWithAdamW(torch.optim.Optimizer):
         self._mdt = momentum_dtype
         dev = (muon + adamw)[0].device if (muon or adamw) else torch.device("cuda")
         self._ctx = B.muon_init(dev.index if dev.index is not None else torch.cuda.current_device())
-        self._adamw_step = 0
         self._ws = None
         self._ws_bytes = 0
         for p in muon:
@@ -104,6 +116,7 @@ class MuonWithAdamW(torch.optim.Optimizer):
         for p in adamw:
             self.state[p]["m"] = torch.zeros_like(p, dtype=torch.float32)
             self.state[p]["v"] = torch.zeros_like(p, dtype=torch.float32)
+            self.state[p]["step"] = 0
 
     def _workspace(self, nbytes: int, device) -> int:
         if self._ws is None or self._ws_bytes < nbytes:
@@ -133,16 +146,18 @@ class MuonWithAdamW(torch.optim.Optimizer):
             nbytes = B.muon_workspace_size(self._ctx, mats, hp)
             ws = self._workspace(nbytes, ps[0].device)
             B.check(B.muon_step(self._ctx, mats, hp, ws, nbytes, stream), "muon_step")
-        # AdamW: one call per (weight dtype, gradient dtype), all tensors of it together.
-        self._adamw_step += 1
-        by_dtype = {}
+        # AdamW: one call per (weight dtype, gradient dtype, step count), all tensors of it
+        # together (normally every tensor has taken every step: one call per dtype pair).
+        by_key = {}
         for p in adamw_group["params"]:
             if p.grad is None:
                 continue
-            by_dtype.setdefault((_dtype_name(p.dtype), _dtype_name(p.grad.dtype)), []).append(p)
-        for (wd, gd), ps in by_dtype.items():
-            hp = B.make_adamw_hparams(**{**self._adamw_hp, "lr": adamw_group.get("adamw_lr", self._adamw_hp["lr"])},
-                                      step=self._adamw_step, w_dtype=wd, g_dtype=gd)
+            self.state[p]["step"] += 1
+            key = (_dtype_name(p.dtype), _dtype_name(p.grad.dtype), self.state[p]["step"])
+            by_key.setdefault(key, []).append(p)
+        for (wd, gd, t), ps in by_key.items():
+            hp = B.make_adamw_hparams(**{**self._adamw_hp, "lr": adamw_group["lr"]},
+                                      step=t, w_dtype=wd, g_dtype=gd)
             ts = [(p, p.grad, self.state[p]["m"], self.state[p]["v"]) for p in ps]
             B.check(B.muon_adamw_step(self._ctx, ts, hp, stream), "muon_adamw_step")
         return loss

@@ -223,8 +223,8 @@ int muon_plan_info(muon_ctx *ctx, const muon_matrix *mats, int count,
  * 0 = 64x64, 1 = 128x128, 2 = 256x128 (kind 2 only), 3 = 256x256; with direct global->LDS
  * loads: 4 = 64x64, 5 = 128x128, 6 = 256x128 (kind 2 only), 7 = 256x256, 8 = 256x256 with
  * 4 waves, 9 = 64x64 and 10 = 128x128 with two k-groups, 11 = 256x256 with 64-byte K
- * slices, 12 = 128x128 with two k-groups and 64-byte K slices; 2, 3, 6, 7, 8 and 11 not
- * fp32);
+ * slices, 12 = 128x128 with two k-groups and 64-byte K slices, 13 = 256x192 (kind 2 only);
+ * 2, 3, 6, 7, 8, 11 and 13 not fp32);
  * an unavailable combination returns MUON_ERR_UNSUPPORTED.
  * Leading dimensions equal the column counts; M, N, K must be multiples of 64. */
 int muon_debug_gemm(muon_ctx *ctx, int kind, int ns_dtype, int tile, int64_t M, int64_t N,

@@ -345,8 +345,8 @@ void set_sym_tiles(GemmParams& p, int64_t Mp, int cfg) {
 
 // Launch a GEMM stage with the tile configuration measured for it. On the first launch
 // of a (stage, path, shape, batch) the candidates are timed on the stage's own buffers
-// (one warm-up and one timed launch each; the stream is synchronised for it) and the
-// fastest is cached in the context; MUON_FLAG_MODEL_ONLY keeps the static choice. A
+// (one warm-up and four timed launches each; the stream is synchronised for it) and the
+// fastest is cached process-wide; MUON_FLAG_MODEL_ONLY keeps the static choice. A
 // stage that updates W is timed through its apply twin, which writes only workspace.
 // Measured tile configurations, shared by every context of the process:
 // (device, stage, path, padded m', padded n' or m', batch) -> TileCfg.
@@ -407,9 +407,13 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
       if (it != g_tuned.end()) { cfg = it->second; found = true; }
     }
     if (!found) {
-      // Each candidate: one warm-up and two timed launches, its time the faster of the two.
-      // The first candidate (in the order below) within 2% of the fastest wins, so that
-      // near-ties resolve the same way from run to run.
+      // Each candidate: one warm-up and four timed launches, its time the fastest of them.
+      // The timed launches run in four passes over the candidates, alternately in forward
+      // and in reverse order: back-to-back MFMA work lowers the clock under the power limit
+      // within milliseconds, so passes in one fixed order would favour the first
+      // candidates, and single launches vary by several percent. The first candidate (in
+      // the order below) within 2% of the fastest wins, so that near-ties resolve the same
+      // way from run to run.
       std::vector<int> cands;
       if (env.f32) {
         cands = {TILE_64, TILE_128, TILE_64_DMA, TILE_128_DMA, TILE_128_DMA_K2};
@@ -421,17 +425,22 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
         if (g.Mp >= 256) {
           cands.push_back(TILE_256x128_DMA);
           cands.push_back(TILE_256_DMA);
+          cands.push_back(TILE_256x192_DMA);
         }
       }
       for (int i = 0; i < 2; ++i)
         if (!ctx->tune_ev[i] && hipEventCreate(&ctx->tune_ev[i]) != hipSuccess) return hipErrorUnknown;
       const GemmOp top = (op == OP_UPDATE) ? OP_APPLY : op;
       std::vector<float> times(cands.size(), 1e30f);
-      for (size_t ci = 0; ci < cands.size(); ++ci) {
-        const int c = cands[ci];
-        const GemmParams p = build(c);
-        if (launch_gemm(top, env.f32, c, p, env.st) != hipSuccess) continue;  // warm-up
-        for (int rep = 0; rep < 2; ++rep) {
+      std::vector<char> ok(cands.size(), 0);
+      for (size_t ci = 0; ci < cands.size(); ++ci)  // warm-up; a configuration that fails to launch is skipped
+        ok[ci] = launch_gemm(top, env.f32, cands[ci], build(cands[ci]), env.st) == hipSuccess;
+      for (int pass = 0; pass < 4; ++pass) {
+        for (size_t k = 0; k < cands.size(); ++k) {
+          const size_t ci = pass % 2 == 0 ? k : cands.size() - 1 - k;
+          if (!ok[ci]) continue;
+          const int c = cands[ci];
+          const GemmParams p = build(c);
           if (hipEventRecord(ctx->tune_ev[0], env.st) != hipSuccess) return hipErrorUnknown;
           if (launch_gemm(top, env.f32, c, p, env.st) != hipSuccess) return hipErrorUnknown;
           if (hipEventRecord(ctx->tune_ev[1], env.st) != hipSuccess) return hipErrorUnknown;

@@ -752,6 +752,9 @@ hipError_t launch_tile(int cfg, const GemmParams& p, hipStream_t st) {
       if constexpr (KIND != KIND_F32) return launch_dma<KIND, 256, 256, 2, 4, 4, SYM, EPI, TAG, 1, 4>(p, st);
       return hipErrorInvalidValue;
     case TILE_128_DMA_K2_H: return launch_dma<KIND, 128, 128, 2, 2, 8, SYM, EPI, TAG, 2, 4>(p, st);
+    case TILE_256x192_DMA:  // 8 waves, wave tile 64 x 96: 2560 x 9728 is 510 tiles, two full rounds of 256 CUs
+      if constexpr (!SYM && KIND != KIND_F32) return launch_dma<KIND, 256, 192, 4, 2, 2, SYM, EPI, TAG>(p, st);
+      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

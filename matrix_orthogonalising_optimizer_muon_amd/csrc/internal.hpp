@@ -58,7 +58,7 @@ enum GemmOp : int {
 };
 
 // Workgroup tile configurations. Symmetric-output stages need BM == BN. Configurations
-// 0-3 stage operands through registers; 4-12 use the CDNA4 direct global -> LDS loads
+// 0-3 stage operands through registers; 4-13 use the CDNA4 direct global -> LDS loads
 // with a multi-stage LDS ring.
 enum TileCfg : int {
   TILE_64 = 0,           // 64 x 64, 4 waves, wave tile 32 x 32
@@ -74,14 +74,15 @@ enum TileCfg : int {
   TILE_128_DMA_K2 = 10,  // as TILE_128_DMA with 8 waves: two k-groups split every slice
   TILE_256_DMA_H = 11,   // as TILE_256_DMA with 64-byte slices: 4 LDS stages
   TILE_128_DMA_K2_H = 12,  // as TILE_128_DMA_K2 with 64-byte slices: 8 LDS stages
-  TILE_COUNT = 13
+  TILE_256x192_DMA = 13,  // 256 x 192, 8 waves, wave tile 64 x 96, 2 LDS stages
+  TILE_COUNT = 14
 };
 inline int tile_bm(int cfg) {
-  static const int bm[TILE_COUNT] = {64, 128, 256, 256, 64, 128, 256, 256, 256, 64, 128, 256, 128};
+  static const int bm[TILE_COUNT] = {64, 128, 256, 256, 64, 128, 256, 256, 256, 64, 128, 256, 128, 256};
   return bm[cfg];
 }
 inline int tile_bn(int cfg) {
-  static const int bn[TILE_COUNT] = {64, 128, 128, 256, 64, 128, 128, 256, 256, 64, 128, 256, 128};
+  static const int bn[TILE_COUNT] = {64, 128, 128, 256, 64, 128, 128, 256, 256, 64, 128, 256, 128, 192};
   return bn[cfg];
 }
 

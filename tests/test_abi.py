@@ -170,7 +170,7 @@ def test_debug_gemm_validation(hctx):
     P = ctypes.c_void_p(FAKE)
     # f(ctx, kind, ns_dtype, tile_cfg, M, N, K, A, B, E, C, C2, alpha, beta, gamma, oscale, stream)
     assert f(hctx, 3, 1, 0, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
-    assert f(hctx, 0, 1, 13, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 0, 1, 14, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
     assert f(hctx, 0, 1, 6, 256, 256, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
     assert f(hctx, 0, 1, 0, 64, 64, 100, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
     assert f(hctx, 1, 1, 0, 64, 128, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
@@ -279,7 +279,7 @@ def test_tune_cache_round_trip(hctx, tmp_path):
     "2 1 2560 9728 1 7\n",          # 256 tile on the fp32 path
     "2 0 2500 9728 1 1\n",          # not a multiple of 64
     "2 0 2560 9728 0 1\n",          # empty batch
-    "2 0 2560 9728 1 13\n",         # unknown tile
+    "2 0 2560 9728 1 14\n",         # unknown tile
     "2 0 2560 9728 1 x\n",
 ])
 def test_tune_cache_rejects_bad_files(hctx, tmp_path, text):

@@ -60,7 +60,7 @@ def check_elems(got, ref, K, u_out):
 # 4-7: the same tiles with direct global -> LDS loads; 8: 256x256 with 4 waves; 9, 10:
 # 64 and 128 tiles with two k-groups; 11, 12: 256 and 128 (two k-groups) with 64-byte slices
 SYM_TILES = [0, 1, 3, 4, 5, 7, 8, 9, 10, 11, 12]
-ALL_TILES = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12]
+ALL_TILES = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13]
 F32_TILES = [0, 1, 4, 5, 9, 10, 12]
 
 
@@ -172,3 +172,6 @@ def test_unavailable_tile_config(B, ctx):
     assert B.muon_debug_gemm(ctx, 0, "f32", 3, 64, 64, 64, X, None, None, X) == B.MUON_ERR_UNSUPPORTED
     assert B.muon_debug_gemm(ctx, 2, "f32", 2, 64, 64, 64, X, X, None, X) == B.MUON_ERR_UNSUPPORTED
     assert B.muon_debug_gemm(ctx, 0, "bf16", 2, 64, 64, 64, X, None, None, X) == B.MUON_ERR_ARG
+    Y = torch.zeros((256, 256), dtype=torch.float32, device="cuda")
+    assert B.muon_debug_gemm(ctx, 0, "bf16", 13, 256, 256, 64, Y, None, None, Y) == B.MUON_ERR_ARG
+    assert B.muon_debug_gemm(ctx, 2, "f32", 13, 256, 192, 64, Y, Y, None, Y) == B.MUON_ERR_UNSUPPORTED

@@ -85,6 +85,7 @@ struct Group {
   int64_t stride_x = 0, stride_sq = 0;
   int mom_tiles_m = 0, mom_tiles_n = 0;
   bool single_wg = false;      // whole update per matrix in one workgroup (small shapes)
+  bool has_tall = false;       // some member is stored transposed (rows > cols)
   double work = 0.0;
   muon_hparams hs{};           // the call's hparams with this group's mode and schedule
 };
@@ -212,6 +213,7 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
       g.m = m; g.n = n;
       g.Mp = round_up(m, kPad); g.Np = round_up(n, kPad);
       g.members.assign(all.begin() + b, all.begin() + std::min(all.size(), b + kMaxBatch));
+      for (int i : g.members) g.has_tall = g.has_tall || mats[i].rows > mats[i].cols;
       const int64_t cnt = static_cast<int64_t>(g.members.size());
       g.hs = hp;
       if (hp.mode == MUON_NS_AUTO_SCHEDULE) choose_schedule(ctx, g, hp, f32);
@@ -635,6 +637,7 @@ int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
   mp.mu = hp.momentum; mp.nesterov = hp.nesterov;
   mp.g_bf16 = hp.g_dtype == MUON_BF16; mp.m_bf16 = hp.m_dtype == MUON_BF16; mp.u_bf16 = !f32;
   mp.partials = reinterpret_cast<float*>(env.ws + g.off_partials);
+  mp.has_tall = g.has_tall ? 1 : 0;
   {
     // algorithmic bytes: G read, M read + write, U written
     const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;

@@ -111,6 +111,7 @@ struct MomentumParams {
   int32_t nesterov;
   int32_t g_bf16, m_bf16, u_bf16;   // storage dtypes (0: fp32)
   float* partials;        // [count][tiles_m*tiles_n]
+  int32_t has_tall;       // some matrix of the batch is stored transposed (rows > cols)
 };
 hipError_t launch_momentum(const MomentumParams& p, hipStream_t st);
 

@@ -211,6 +211,19 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
   }
 }
 
+// Epilogue chunks: CR block rows x CC block columns of a wave's FM x FN blocks, holding
+// at most V loaded values (16 per block) per lane, CR and CC dividing FM and FN.
+constexpr int largest_divisor_le(int n, int cap) {
+  int best = 1;
+  for (int d = 1; d <= n; ++d)
+    if (n % d == 0 && d <= cap) best = d;
+  return best;
+}
+constexpr int chunk_cols(int FN, int V) { return FN * 16 <= V ? FN : largest_divisor_le(FN, V / 16); }
+constexpr int chunk_rows(int FM, int FN, int V) {
+  return FN * 16 <= V ? largest_divisor_le(FM, V / (FN * 16)) : 1;
+}
+
 // Epilogue shared by both kernels: per 32x32 block a lane holds column c and rows
 // r0..r0+3 for q = 0..3 (acc[i][j][4q + e] is row r0 + e).
 // The W update loads every W value of a chunk of block rows before computing and storing
@@ -232,18 +245,24 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
   if (EPI == EPI_APPLY && p.C2 != nullptr) C2 = static_cast<TO*>(p.C2) + static_cast<int64_t>(mat) * p.sC2;
   if (has_e) E = static_cast<const TO*>(p.E) + static_cast<int64_t>(mat) * p.sE;
 
-  // v = alpha acc + beta E + gamma I for rows r0..r0+3 of column c of block (i, j).
-  auto value = [&](int i, int j, int q, int r0, int c, float (&v)[4]) {
+  // E at rows r0..r0+3 of column c (the caller keeps r0 < M and c < N).
+  auto load_e = [&](int r0, int c, float* ev) {
+    if (p.e_trans) {
+      float t[4];
+      load4(E + static_cast<int64_t>(c) * p.lde + r0, t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ev[e] = t[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ev[e] = from_out(E[static_cast<int64_t>(r0 + e) * p.lde + c]);
+    }
+  };
+  // v = alpha acc + beta E + gamma I for rows r0..r0+3 of column c of block (i, j), with E
+  // already loaded into ev.
+  auto value_ev = [&](int i, int j, int q, int r0, int c, const float* ev, float (&v)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][q * 4 + e];
     if (has_e) {
-      float ev[4];
-      if (p.e_trans) {
-        load4(E + static_cast<int64_t>(c) * p.lde + r0, ev);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ev[e] = from_out(E[static_cast<int64_t>(r0 + e) * p.lde + c]);
-      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += beta * ev[e];
     }
@@ -257,8 +276,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
     const float decay = 1.0f - p.lr * p.wd;
     const bool vec = w_vec(p, d);
     constexpr int WB = (WM * WN >= 8) ? 32 : 64;  // W values per lane per chunk
-    constexpr int IG = (FN * 16 >= WB) ? 1 : ((WB / (FN * 16)) < FM ? WB / (FN * 16) : FM);
-    static_assert(FM % IG == 0, "update chunk");
+    constexpr int IG = (FN * 16 >= WB) ? 1 : largest_divisor_le(FM, WB / (FN * 16));
 #pragma unroll
     for (int i0 = 0; i0 < FM; i0 += IG) {
       float w[IG][FN][16];
@@ -282,30 +300,62 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
           for (int q = 0; q < 4; ++q) {
             const int r0 = m0 + wm0 + (i0 + ii) * 32 + q * 8 + (lane >> 5) * 4;
             if (r0 >= p.M || c >= p.N) continue;
+            // The E term (plain NS: a X) is loaded here, after the chunk's W loads: loading
+            // it with them measured slower on the 2048 x 2048 plain-NS update.
+            float ev[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (has_e) load_e(r0, c, ev);
             float v[4];
-            value(i0 + ii, j, q, r0, c, v);
+            value_ev(i0 + ii, j, q, r0, c, ev, v);
             w_store4(p, d, vec, decay, r0, c, &w[ii][j][4 * q], v);
           }
         }
     }
   } else {
+    // With an E term, every E value of a chunk of block rows is loaded before any of the
+    // chunk's stores: the compiler cannot tell C from E, so a load placed after a store
+    // waits for it, and block by block each wave would pay one memory round trip per block.
+    // E values per lane per chunk: 64 for 4-wave tiles, 48 for 8-wave tiles, one block (16)
+    // for 128 x 128 wave tiles, whose accumulators fill the register file.
+    constexpr int EB = FM * FN >= 16 ? 16 : (WM * WN >= 8 ? 48 : 64);
+    constexpr int EG = chunk_rows(FM, FN, EB), EJ = chunk_cols(FN, EB);
+    const float os = (EPI == EPI_APPLY) ? p.oscale : 1.0f;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i0 = 0; i0 < FM; i0 += EG)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int c = n0 + wn0 + j * 32 + (lane & 31);
+    for (int j0 = 0; j0 < FN; j0 += EJ) {
+      float ev[EG][EJ][16];
+      if (has_e) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r0 = m0 + wm0 + i * 32 + q * 8 + (lane >> 5) * 4;
-          // M and N are multiples of 4: rows r0..r0+3 are all in range or all out.
-          if (r0 >= p.M || c >= p.N) continue;
-          float v[4];
-          value(i, j, q, r0, c, v);
-          const float os = (EPI == EPI_APPLY) ? p.oscale : 1.0f;
+        for (int ii = 0; ii < EG; ++ii)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) C[static_cast<int64_t>(r0 + e) * p.ldc + c] = to_out<TO>(v[e] * os);
-          if (SYM && mirror) store4(C + static_cast<int64_t>(c) * p.ldc + r0, v, 1.0f);
-          if (EPI == EPI_APPLY && C2 != nullptr) store4(C2 + static_cast<int64_t>(c) * p.ldc2 + r0, v, os);
+          for (int jj = 0; jj < EJ; ++jj) {
+            const int c = n0 + wn0 + (j0 + jj) * 32 + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r0 = m0 + wm0 + (i0 + ii) * 32 + q * 8 + (lane >> 5) * 4;
+              if (r0 < p.M && c < p.N) load_e(r0, c, &ev[ii][jj][4 * q]);
+            }
+          }
+      }
+#pragma unroll
+      for (int ii = 0; ii < EG; ++ii) {
+        const int i = i0 + ii;
+#pragma unroll
+        for (int jj = 0; jj < EJ; ++jj) {
+          const int j = j0 + jj;
+          const int c = n0 + wn0 + j * 32 + (lane & 31);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r0 = m0 + wm0 + i * 32 + q * 8 + (lane >> 5) * 4;
+            // M and N are multiples of 4: rows r0..r0+3 are all in range or all out.
+            if (r0 >= p.M || c >= p.N) continue;
+            float v[4];
+            value_ev(i, j, q, r0, c, &ev[ii][jj][4 * q], v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) C[static_cast<int64_t>(r0 + e) * p.ldc + c] = to_out<TO>(v[e] * os);
+            if (SYM && mirror) store4(C + static_cast<int64_t>(c) * p.ldc + r0, v, 1.0f);
+            if (EPI == EPI_APPLY && C2 != nullptr) store4(C2 + static_cast<int64_t>(c) * p.ldc2 + r0, v, os);
+          }
         }
       }
     }

@@ -496,6 +496,7 @@ hipError_t square(const Group& g, const StepEnv& env, const void* A, const void*
     p.sA = p.sB = p.sC = p.sE = g.stride_sq;
     p.M = p.N = p.K = static_cast<int32_t>(g.Mp);
     p.alpha = alpha; p.beta = beta; p.gamma = gamma;
+    p.e_from_a = (E != nullptr && E == A) ? 1 : 0;
     set_sym_tiles(p, g.Mp, cfg);
     return p;
   };
@@ -1025,6 +1026,7 @@ int muon_debug_gemm(muon_ctx* ctx, int kind, int ns_dtype, int tile, int64_t M, 
     } else {
       op = kind == 0 ? OP_SYRK_IN : OP_SYM;
       p.ldc = N; p.lde = N;
+      p.e_from_a = (kind == 1 && E != nullptr && E == A && K == N) ? 1 : 0;
       const int nt = static_cast<int>((M + tile_bm(tile) - 1) / tile_bm(tile));
       p.tiles_m = p.tiles_n = nt;
       p.tiles = nt * (nt + 1) / 2;

@@ -231,7 +231,8 @@ constexpr int chunk_rows(int FM, int FN, int V) {
 // holds at most 64 (8-wave tiles: 32) W values per lane to stay within the register file.
 template <int KIND, int BM, int BN, int WM, int WN, bool SYM, int EPI, int FM, int FN, typename TO>
 __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][FN], int mat, int tm,
-                                         int tn, int m0, int n0, int wm0, int wn0, int lane) {
+                                         int tn, int m0, int n0, int wm0, int wn0, int lane,
+                                         const float* ecap = nullptr, bool use_cap = false) {
   const float alpha = scaled(p.alpha, p.s, mat, p.alpha_spow);
   const float beta = scaled(p.beta, p.s, mat, p.beta_spow);
   const float gamma = p.gamma;
@@ -324,7 +325,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
 #pragma unroll
     for (int j0 = 0; j0 < FN; j0 += EJ) {
       float ev[EG][EJ][16];
-      if (has_e) {
+      if (has_e && use_cap) {
+        // E was read from LDS during the main loop (gemm_dma_kernel, E = A)
+#pragma unroll
+        for (int ii = 0; ii < EG; ++ii)
+#pragma unroll
+          for (int jj = 0; jj < EJ; ++jj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ev[ii][jj][e] = ecap[((i0 + ii) * FN + j0 + jj) * 16 + e];
+      } else if (has_e) {
 #pragma unroll
         for (int ii = 0; ii < EG; ++ii)
 #pragma unroll
@@ -466,6 +475,35 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   const int nk = p.K / BK;
   const int kk0 = kgrp * KL;
 
+  // E = A (the P epilogue of R^2 and A^2, square products): the slice of A holding K
+  // columns n0 + wn0 .. n0 + wn0 + TWN - 1 (one slice: BK == TWN) carries exactly the E
+  // values of this wave's output block (E(r, c) = A(r, c)), so they are read from LDS while
+  // that slice is resident instead of from global memory in the epilogue. Only the waves
+  // that run the epilogue (k-group 0) capture; a wave whose columns lie past N stores
+  // nothing and captures nothing.
+  constexpr bool CAP = SYM && EPI == EPI_STORE && KIND == KIND_F16 && BK == TWN && FM * FN <= 4;
+  static_assert(!CAP || KL % 2 == 0, "the capture split is written for an even k-step count");
+  float ecap[CAP ? FM * FN * 16 : 1];
+  const bool cap = CAP && p.e_from_a && kgrp == 0 && n0 + wn0 < p.N;
+  auto capture = [&](int kt) {
+    if constexpr (CAP) {
+      const unsigned short* la16 = reinterpret_cast<const unsigned short*>(lds + (kt % NS) * STAGE);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int k = j * 32 + (lane & 31);  // column within the slice
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int row = wm0 + i * 32 + q * 8 + (lane >> 5) * 4 + e;
+              ecap[(i * FN + j) * 16 + q * 4 + e] = f16_to_f32(la16[swz_ch<CH>(row, k >> 3) * 8 + (k & 7)]);
+            }
+        }
+    }
+  };
+
   u32x4 fa[2][FM], fb[2][FN];
   auto load_frags = [&](int buf, const u32x4* la, const u32x4* lb, int kk) {
     const int ch = 2 * kk + (lane >> 5);
@@ -550,8 +588,23 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   using YES = std::true_type;
   using NO = std::false_type;
   if constexpr (KL % 2 == 0) {
-    for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, I0{}, YES{});
-    slice(nk - 1, I0{}, NO{});
+    if (CAP && cap) {
+      // The same slices and barriers as below, with the E reads before slice kcap. Slice
+      // kcap has landed: the barrier of the slice before it (or of the prologue) waited for it.
+      const int kcap = (n0 + wn0) / BK;  // < nk, as n0 + wn0 < N = K
+      int kt = 0;
+      for (; kt < kcap; ++kt) slice(kt, I0{}, YES{});
+      capture(kcap);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kcap + 1 < nk) {
+        slice(kcap, I0{}, YES{});
+        for (kt = kcap + 1; kt + 1 < nk; ++kt) slice(kt, I0{}, YES{});
+      }
+      slice(nk - 1, I0{}, NO{});
+    } else {
+      for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, I0{}, YES{});
+      slice(nk - 1, I0{}, NO{});
+    }
   } else {
     int kt = 0;
     for (; kt + 2 < nk; kt += 2) {
@@ -599,7 +652,8 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
     if (kgrp != 0) return;
   }
 
-  epilogue<KIND, BM, BN, WM, WN, SYM, EPI, FM, FN, TO>(p, acc, mat, tm, tn, m0, n0, wm0, wn0, lane);
+  epilogue<KIND, BM, BN, WM, WN, SYM, EPI, FM, FN, TO>(p, acc, mat, tm, tn, m0, n0, wm0, wn0, lane,
+                                                        ecap, cap);
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, int PF, bool SYM, int EPI, int TAG>

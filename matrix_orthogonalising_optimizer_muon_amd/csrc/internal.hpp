@@ -42,6 +42,7 @@ struct GemmParams {
   float alpha, beta, gamma, oscale;
   int32_t alpha_spow, beta_spow;
   int32_t e_trans;
+  int32_t e_from_a;       // E is A (same buffer, lde == lda, sE == sA, K == N, !e_trans)
   const float* s;
   const MatDesc* table;   // EPI_UPDATE: descriptors of the batch (entry i = matrix i)
   float lr, wd;

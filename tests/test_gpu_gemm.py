@@ -115,6 +115,29 @@ def test_square_poly(B, ctx, tile, ns, dt, u):
 
 
 @pytest.mark.parametrize("tile", SYM_TILES)
+@pytest.mark.parametrize("M", [576, 1024])
+def test_square_e_is_a_matches_copy(B, ctx, tile, M):
+    """kind 1 with E = A itself (the direct-load kernels with 64-wide wave tiles then read
+    E from A's slices in LDS during the main loop) and with E a separate copy of A: the
+    same values enter the same arithmetic, so the outputs are bitwise equal, and both match
+    the float64 reference. M = 576 leaves waves whose columns lie past the edge."""
+    rng = np.random.default_rng(M + tile)
+    S = rng.standard_normal((M, M)) / np.sqrt(M)
+    S = f16_round((S + S.T) / 2)
+    A = dev(S, torch.float16)
+    A_copy = A.clone()
+    C1 = torch.empty((M, M), dtype=torch.float16, device="cuda")
+    C2 = torch.empty_like(C1)
+    alpha, beta, gamma = -0.75, 2.5, 1.5
+    assert B.muon_debug_gemm(ctx, 1, "bf16", tile, M, M, M, A, A, A, C1, alpha=alpha, beta=beta, gamma=gamma) == 0
+    assert B.muon_debug_gemm(ctx, 1, "bf16", tile, M, M, M, A, A, A_copy, C2, alpha=alpha, beta=beta,
+                             gamma=gamma) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    check_elems(host(C1), alpha * (S @ S.T) + beta * S + gamma * np.eye(M), M, 2.0 ** -11)
+
+
+@pytest.mark.parametrize("tile", SYM_TILES)
 @pytest.mark.parametrize("M,K", [(128, 576), (320, 192)])
 def test_sym_long_fp16(B, ctx, tile, M, K):
     """kind 1 with A = B = X (M x K, K != M): the Gram product of the fp16 iterate."""

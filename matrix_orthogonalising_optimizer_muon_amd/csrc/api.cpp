@@ -587,7 +587,13 @@ bool ensure_lanes(muon_ctx* ctx, int n) {
   return true;
 }
 
-int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
+// Groups whose descriptors travel in the momentum kernel's arguments (which then writes
+// them to the table): staged groups of at most kTableChunk matrices.
+bool inline_descs(const Group& g) {
+  return !g.single_wg && g.members.size() <= static_cast<size_t>(kTableChunk);
+}
+
+int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc* host_desc) {
   const muon_hparams& hp = g.hs;   // the group's mode and schedule
   const bool f32 = env.f32;
   void* X = env.ws + g.off_x;
@@ -639,6 +645,11 @@ int run_group(const Group& g, const StepEnv& env, const MatDesc* table) {
   mp.g_bf16 = hp.g_dtype == MUON_BF16; mp.m_bf16 = hp.m_dtype == MUON_BF16; mp.u_bf16 = !f32;
   mp.partials = reinterpret_cast<float*>(env.ws + g.off_partials);
   mp.has_tall = g.has_tall ? 1 : 0;
+  if (inline_descs(g)) {
+    mp.inl.n = count;
+    for (int i = 0; i < count; ++i) mp.inl.d[i] = host_desc[i];
+    mp.table_out = table;
+  }
   {
     // algorithmic bytes: G read, M read + write, U written
     const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;
@@ -834,14 +845,19 @@ int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
         descs[g.table_base + i] = d;
       }
     }
-    for (int b = 0; b < count; b += kTableChunk) {
-      TableChunk c;
-      std::memset(&c, 0, sizeof(c));
-      c.n = std::min(kTableChunk, count - b);
-      for (int i = 0; i < c.n; ++i) c.d[i] = descs[b + i];
-      StageTimer tm(ctx, env.st, ST_TABLE, 0, 0, c.n, 0.0, sizeof(MatDesc) * c.n);
-      MUON_HIP(launch_write_table(c, table + b, env.st));
-      tm.done();
+    // Groups with inline descriptors get their entries from their momentum kernel.
+    for (const Group& g : plan.groups) {
+      if (inline_descs(g)) continue;
+      const int base = g.table_base, n = static_cast<int>(g.members.size());
+      for (int b = 0; b < n; b += kTableChunk) {
+        TableChunk c;
+        std::memset(&c, 0, sizeof(c));
+        c.n = std::min(kTableChunk, n - b);
+        for (int i = 0; i < c.n; ++i) c.d[i] = descs[base + b + i];
+        StageTimer tm(ctx, env.st, ST_TABLE, 0, 0, c.n, 0.0, sizeof(MatDesc) * c.n);
+        MUON_HIP(launch_write_table(c, table + base + b, env.st));
+        tm.done();
+      }
     }
     // Independent shape groups run on up to kMaxLanes streams (largest work first, each
     // to the least loaded lane) when none of them still has tiles to measure and the
@@ -853,7 +869,7 @@ int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
     if (nl > 1 && !ensure_lanes(ctx, nl)) nl = 1;
     if (nl == 1) {
       for (const Group& g : plan.groups) {
-        const int r = run_group(g, env, table + g.table_base);
+        const int r = run_group(g, env, table + g.table_base, descs.data() + g.table_base);
         if (r != MUON_OK) return r;
       }
       return MUON_OK;
@@ -867,7 +883,7 @@ int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
       load[l] += g.work;
       StepEnv le = env;
       if (l > 0) le.st = ctx->lanes[l - 1];
-      r = run_group(g, le, table + g.table_base);
+      r = run_group(g, le, table + g.table_base, descs.data() + g.table_base);
       if (r != MUON_OK) break;
     }
     // The caller's stream waits for every lane, also after a failed launch, so nothing

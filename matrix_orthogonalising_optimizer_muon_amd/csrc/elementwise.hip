@@ -164,7 +164,8 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const MomentumParams
   __shared__ float wsum[kThreads / 64];
 
   const int mat = blockIdx.y;
-  const MatDesc d = p.table[mat];
+  const MatDesc d = p.inl.n > 0 ? p.inl.d[mat] : p.table[mat];
+  if (p.inl.n > 0 && blockIdx.x == 0 && threadIdx.x == 0) p.table_out[mat] = d;
   const int tid = threadIdx.x;
   // 16-byte accesses when every row start is 16-byte aligned (row length a multiple of
   // 8 elements and aligned base pointers); otherwise element by element.
@@ -278,7 +279,8 @@ __global__ __launch_bounds__(kFlatThreads) void momentum_flat_kernel(const Momen
   __shared__ float wsum[kFlatThreads / 64];
   const int mat = blockIdx.y;
   const int t = blockIdx.x;
-  const MatDesc d = p.table[mat];
+  const MatDesc d = p.inl.n > 0 ? p.inl.d[mat] : p.table[mat];
+  if (p.inl.n > 0 && blockIdx.x == 0 && threadIdx.x == 0) p.table_out[mat] = d;
   const int tid = threadIdx.x;
   const bool vec_ok = (d.cols % 8) == 0 && (reinterpret_cast<uintptr_t>(d.G) % 16) == 0 &&
                       (reinterpret_cast<uintptr_t>(d.M) % 16) == 0;

@@ -99,6 +99,13 @@ inline bool tile_available(bool sym, bool f32, int cfg) {
 // Launch one batched GEMM stage. ns_f32: fp32 kernels, else bf16/fp16 kernels.
 hipError_t launch_gemm(GemmOp op, bool ns_f32, int cfg, const GemmParams& p, hipStream_t st);
 
+// Copy up to kTableChunk descriptors (passed by value) into device memory.
+constexpr int kTableChunk = 48;
+struct TableChunk {
+  MatDesc d[kTableChunk];
+  int32_t n;
+};
+
 // Momentum + canonical-orientation write of U + per-block partial sums of U^2.
 struct MomentumParams {
   const MatDesc* table;   // entry i = matrix i of the batch
@@ -113,6 +120,11 @@ struct MomentumParams {
   int32_t g_bf16, m_bf16, u_bf16;   // storage dtypes (0: fp32)
   float* partials;        // [count][tiles_m*tiles_n]
   int32_t has_tall;       // some matrix of the batch is stored transposed (rows > cols)
+  // With inl.n > 0 (batches of at most kTableChunk matrices) the descriptors come in the
+  // kernel arguments and workgroup (0, i) also writes entry i to table_out, for the later
+  // stages of the batch; no separate table launch is needed.
+  TableChunk inl;
+  MatDesc* table_out;
 };
 hipError_t launch_momentum(const MomentumParams& p, hipStream_t st);
 
@@ -180,12 +192,6 @@ struct AdamChunk {
 int64_t adam_blocks(int64_t numel);
 hipError_t launch_adamw(const AdamChunk& c, int64_t blocks, hipStream_t st);
 
-// Copy up to kTableChunk descriptors (passed by value) into device memory.
-constexpr int kTableChunk = 48;
-struct TableChunk {
-  MatDesc d[kTableChunk];
-  int32_t n;
-};
 hipError_t launch_write_table(const TableChunk& c, MatDesc* dst, hipStream_t st);
 
 }  // namespace muon

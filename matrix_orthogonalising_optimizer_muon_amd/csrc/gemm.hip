@@ -229,15 +229,24 @@ constexpr int chunk_rows(int FM, int FN, int V) {
 // The W update loads every W value of a chunk of block rows before computing and storing
 // them, so a wave pays one memory round trip per chunk instead of one per block; a chunk
 // holds at most 64 (8-wave tiles: 32) W values per lane to stay within the register file.
-template <int KIND, int BM, int BN, int WM, int WN, bool SYM, int EPI, int FM, int FN, typename TO>
+template <int KIND, int BM, int BN, int WM, int WN, bool SYM, int EPI, int FM, int FN, typename TO,
+          bool STG = false>
 __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][FN], int mat, int tm,
                                          int tn, int m0, int n0, int wm0, int wn0, int lane,
-                                         const float* ecap = nullptr, bool use_cap = false) {
+                                         const float* ecap = nullptr, bool use_cap = false,
+                                         unsigned short* stg = nullptr) {
   const float alpha = scaled(p.alpha, p.s, mat, p.alpha_spow);
   const float beta = scaled(p.beta, p.s, mat, p.beta_spow);
   const float gamma = p.gamma;
   const bool has_e = p.E != nullptr;
   const bool mirror = SYM && (tm != tn);
+  // Staged transposed output of the apply (the direct-load kernels pass their LDS, 16-bit
+  // outputs): block of TWN rows of TWM values per wave, rows SPITCH values apart (16-byte
+  // aligned).
+  constexpr int TWM = BM / WM, TWN = BN / WN;
+  constexpr int SPITCH = TWM + 8;
+  constexpr bool STAGED = STG && sizeof(TO) == 2 && EPI == EPI_APPLY && !SYM;
+  const bool tout = (SYM && mirror) || (EPI == EPI_APPLY && p.C2 != nullptr);
 
   TO* C = nullptr;
   TO* C2 = nullptr;
@@ -362,8 +371,39 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
             value_ev(i, j, q, r0, c, &ev[ii][jj][4 * q], v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) C[static_cast<int64_t>(r0 + e) * p.ldc + c] = to_out<TO>(v[e] * os);
-            if (SYM && mirror) store4(C + static_cast<int64_t>(c) * p.ldc + r0, v, 1.0f);
-            if (EPI == EPI_APPLY && C2 != nullptr) store4(C2 + static_cast<int64_t>(c) * p.ldc2 + r0, v, os);
+            if constexpr (STAGED) {
+              // the same rounded values, transposed, into the wave's LDS block (8 bytes)
+              if (tout) store4(stg + (j * 32 + (lane & 31)) * SPITCH + i * 32 + q * 8 + (lane >> 5) * 4, v, os);
+            } else {
+              if (SYM && mirror) store4(C + static_cast<int64_t>(c) * p.ldc + r0, v, 1.0f);
+              if (EPI == EPI_APPLY && C2 != nullptr) store4(C2 + static_cast<int64_t>(c) * p.ldc2 + r0, v, os);
+            }
+          }
+        }
+      }
+    }
+    if constexpr (STAGED) {
+      // The transposed output X'^T of an apply leaves from the wave's LDS block in whole
+      // rows: 16 bytes per lane, TWM / 8 lanes per output row, instead of 8-byte pieces
+      // scattered over 32 rows per instruction. Each wave reads only its own block, which
+      // its own lanes wrote.
+      if (tout) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        TO* dst = C2;
+        const int64_t ld = p.ldc2;
+        constexpr int CPR = TWM / 8;            // 16-byte chunks per output row
+        constexpr int TOTAL = TWN * CPR;
+        static_assert(TOTAL % 64 == 0, "whole instructions");
+#pragma unroll
+        for (int t = 0; t < TOTAL / 64; ++t) {
+          const int idx = t * 64 + lane;
+          const int cl = idx / CPR, ch = idx % CPR;
+          const int grow = n0 + wn0 + cl, gcol = m0 + wm0 + ch * 8;
+          if (grow < p.N && gcol < p.M) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(stg + cl * SPITCH + ch * 8);
+            *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(grow) * ld + gcol) = w;
           }
         }
       }
@@ -414,7 +454,13 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   static_assert(NS >= 2 && (KS == 1 || KS == 2), "stages / k-groups");
   static_assert(KS == 1 || (KS / 2) * BM * BN * 4 <= NS * STAGE * 16, "k-group reduction fits in LDS");
 
-  __shared__ u32x4 lds[NS * STAGE];
+  // The apply epilogue reuses the LDS for its staged transposed output (X'^T, 16-bit kinds):
+  // one block of TWN rows x (TWM + 8) values per wave of k-group 0. (Staging the mirror
+  // tile of the symmetric products the same way measured slightly slower: 28.7 -> 29.1 us
+  // for the 2560 squares, against 133.5 -> 128.6 us for the 2560 x 9728 apply.)
+  constexpr bool STG = KIND != KIND_F32 && EPI == EPI_APPLY && !SYM;
+  constexpr int STG_U32X4 = STG ? (NWC * TWN * (TWM + 8) * 2 + 15) / 16 : 0;
+  __shared__ u32x4 lds[NS * STAGE > STG_U32X4 ? NS * STAGE : STG_U32X4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -649,11 +695,15 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
             for (int e = 0; e < 16; ++e) acc[i][j][e] += r[((i * FN + j) * 16 + e) * (64 * NWC) + wloc * 64 + lane];
       }
     }
+    if constexpr (STG) __syncthreads();  // every wave is done with the partials before the epilogue reuses the LDS
     if (kgrp != 0) return;
+  } else if constexpr (STG) {
+    __syncthreads();  // every wave is done with the last slice before the epilogue reuses the LDS
   }
 
-  epilogue<KIND, BM, BN, WM, WN, SYM, EPI, FM, FN, TO>(p, acc, mat, tm, tn, m0, n0, wm0, wn0, lane,
-                                                        ecap, cap);
+  epilogue<KIND, BM, BN, WM, WN, SYM, EPI, FM, FN, TO, STG>(
+      p, acc, mat, tm, tn, m0, n0, wm0, wn0, lane, ecap, cap,
+      reinterpret_cast<unsigned short*>(lds) + wloc * TWN * (TWM + 8));
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, int PF, bool SYM, int EPI, int TAG>

@@ -343,7 +343,9 @@ __global__ __launch_bounds__(kFinThreads) void norm_finalize_kernel(const float*
 
 // 64 x 64 tile transpose through LDS: coalesced reads of U rows, coalesced writes of
 // X^T rows; the value is scaled by scale * s[mat] and converted (bf16 -> fp16 path).
-__global__ __launch_bounds__(kThreads) void transpose_scale_kernel(const TransposeParams p) {
+constexpr int kTransThreads = 512;  // 8 threads per 64-element row: the whole tile in one pass
+__global__ __launch_bounds__(kTransThreads) void transpose_scale_kernel(const TransposeParams p) {
+  constexpr int kRowsPerPass = kTransThreads / 8;
   __shared__ float tile[kTile][kTile + 1];
   const int mat = blockIdx.y;
   const int tiles_n = p.Np / kTile;
@@ -354,8 +356,8 @@ __global__ __launch_bounds__(kThreads) void transpose_scale_kernel(const Transpo
   const float sc = p.scale * p.s[mat];
   const int64_t ubase = static_cast<int64_t>(mat) * p.sU;
 #pragma unroll
-  for (int pass = 0; pass < kTile / 32; ++pass) {
-    const int lr = cr + pass * 32;
+  for (int pass = 0; pass < kTile / kRowsPerPass; ++pass) {
+    const int lr = cr + pass * kRowsPerPass;
     float v[8];
     load8(p.U, ubase + static_cast<int64_t>(i0 + lr) * p.Np + j0 + cc, p.u_bf16, v);
 #pragma unroll
@@ -364,8 +366,8 @@ __global__ __launch_bounds__(kThreads) void transpose_scale_kernel(const Transpo
   __syncthreads();
   const int64_t xbase = static_cast<int64_t>(mat) * p.sXT;
 #pragma unroll
-  for (int pass = 0; pass < kTile / 32; ++pass) {
-    const int lr = cr + pass * 32;   // row of X^T = column of U
+  for (int pass = 0; pass < kTile / kRowsPerPass; ++pass) {
+    const int lr = cr + pass * kRowsPerPass;   // row of X^T = column of U
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tile[cc + e][lr];
@@ -412,7 +414,7 @@ hipError_t launch_norm_finalize(const float* partials, int per_matrix, int count
 hipError_t launch_transpose_scale(const TransposeParams& p, hipStream_t st) {
   if (p.count <= 0) return hipSuccess;
   dim3 grid((p.Mp / kTile) * (p.Np / kTile), p.count);
-  hipLaunchKernelGGL(transpose_scale_kernel, grid, dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(transpose_scale_kernel, grid, dim3(kTransThreads), 0, st, p);
   return hipGetLastError();
 }
 

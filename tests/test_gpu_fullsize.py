@@ -114,6 +114,8 @@ def run_and_check(run, idx, steps):
             else:
                 assert rel(M_gpu, M_new) <= (s + 1) * 2.0 ** -8, (w.name, spec.name, s)
             W_o[i], M_o[i] = W_new, M_new
+            if len(idx) > 16:  # the long seeded-sample runs report each matrix as it is checked
+                print(f"[fullsize] {w.name} step {s}: {spec.name} O error {e:.3e}", flush=True)
         print(f"[fullsize] {w.name} step {s}: {len(idx)} matrices checked, worst O error {worst:.3e}",
               flush=True)
     return worst

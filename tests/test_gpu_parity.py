@@ -266,6 +266,21 @@ def test_small_shapes_both_paths(B, ctx, ctx_staged, mode):
     assert e1 <= 2e-2 and e2 <= 2e-2
 
 
+@pytest.mark.parametrize("n", [48, 49])
+@pytest.mark.parametrize("tall", [False, True])
+def test_group_descriptor_paths(B, ctx_staged, n, tall):
+    """A same-shape group of 48 matrices takes its descriptors in the momentum kernel's
+    arguments (the kernel writes them to the workspace table for the later stages), one of
+    49 from a table kernel; wide-only groups run the flat momentum kernel, groups with tall
+    members the tiled one. Staged path, two steps, every matrix against the oracle."""
+    shapes = [(96, 64) if tall and k % 3 == 0 else (64, 96) for k in range(n)]
+    w = wl.custom("desc_paths", shapes, structure="gaussian", wid=230 + n + (100 if tall else 0), steps=2)
+    raw = [(0, 0, 0, r, c) for r, c in shapes]
+    hp = B.make_hparams(mode="gram")
+    assert all(B.muon_plan_info(ctx_staged, raw, hp, i).single_wg == 0 for i in range(n))
+    assert check_step(B, ctx_staged, w, mode="gram", steps=2) <= 2e-2
+
+
 @pytest.mark.parametrize("segments", [(2, 3), (1, 1, 1, 1, 1), (3, 2), (1, 3, 1)])
 def test_small_shapes_schedules(B, ctx, segments):
     w = wl.custom("small_sched", [(96, 320), (128, 512)], structure="gaussian", wid=214)

@@ -325,6 +325,15 @@ def main():
         "momentum_gbs": None if mom_gbs is None else round(mom_gbs, 1),
         "momentum_frac_of_hbm": None if mom_gbs is None else round(mom_gbs / HBM_PEAK_GBS, 4),
         "profiled_ms_per_step": round(prof_ms, 4),
+        # per stage and shape group, from the profiled pass: launches per step, average
+        # launch time (us, hipEvents on the launch stream), achieved TFLOP/s or GB/s
+        "stages": [{"stage": e["stage"], "group": f"{e['m']}x{e['n']}x{e['count']}", "tile": e["tile"],
+                    "launches_per_step": round(e["launches"] / args.steps, 2),
+                    "avg_us": round(e["total_ms"] / e["launches"] * 1e3, 2),
+                    **({"tflops": round(e["flops"] / (e["total_ms"] * 1e-3) / 1e12, 1)} if e["flops"] else {}),
+                    **({"gbs": round(e["bytes"] / (e["total_ms"] * 1e-3) / 1e9, 1)}
+                       if e["bytes"] and not e["flops"] else {})}
+                   for e in prof],
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

@@ -36,7 +36,9 @@ repeated where it is used):
 * the weight update is ``W' = W*(1 - lr*wd) - lr*O`` (decoupled decay, no extra scale).
 
 Pins: ``tests/test_oracle.py`` checks every function here against closed forms (SVD of
-an odd matrix polynomial, geometric series, rank-one inputs), exact-arithmetic identities
+an odd matrix polynomial, geometric series, rank-one inputs; the Frobenius normalisation
+against singular values read off the spectrum of a rank-two and a full-rank input, where a
+spectral-norm or other scaling gives different values), exact-arithmetic identities
 (Gram = plain for any schedule, transpose and scale invariance), the singular-value band
 the coefficients imply, the polar factor for the classical quintic, brute-force loops on
 tiny inputs, and the FLOP counts the MuonX article prints for a 2560 x 9728 matrix.

@@ -354,3 +354,68 @@ def test_planted_mistakes_are_caught_gram(kind):
         mut = _gram_mutant(kind)(X0, COEFFS, (2, 2, 1))
         err = rel(mut, om.newton_schulz_plain(X0, COEFFS, 5))
     assert not (err <= 1e-6)
+
+
+# ---------------------------------------------------------------- Frobenius normalisation
+
+def _rank_two(m=6, n=10, seed=0):
+    rng = np.random.default_rng(seed)
+    U, _ = np.linalg.qr(rng.standard_normal((m, 2)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, 2)))
+    return (U * np.array([3.0, 4.0])) @ V.T
+
+
+def test_frobenius_normalise_rank_two():
+    """Singular values (3, 4): the Frobenius norm is 5, so X0 has singular values (0.6, 0.8);
+    a spectral-norm scaling would give (0.75, 1). With eps = 5 the divisor is 5 + 5 = 10."""
+    X = _rank_two()
+    s = np.linalg.svd(om.frobenius_normalise(X, 0.0), compute_uv=False)
+    assert np.allclose(s[:2], [0.8, 0.6], rtol=0, atol=1e-15) and np.all(s[2:] < 1e-15)
+    s = np.linalg.svd(om.frobenius_normalise(X, 5.0), compute_uv=False)
+    assert np.allclose(s[:2], [0.4, 0.3], rtol=0, atol=1e-15)
+    s = np.linalg.svd(om.frobenius_normalise(X.T, 0.0), compute_uv=False)   # orientation-free
+    assert np.allclose(s[:2], [0.8, 0.6], rtol=0, atol=1e-15)
+
+
+def normalised_closed_form(G, coeffs, rounds):
+    """O from the raw momentum: with G = U diag(s) V^T, X0 has singular values
+    s / sqrt(sum s^2) (the Frobenius norm read off the spectrum, not computed from the
+    entries) and NS maps them through phi^rounds."""
+    U, s, Vt = np.linalg.svd(np.asarray(G, np.float64), full_matrices=False)
+    return (U * phi_iter(s / np.sqrt(np.sum(s * s)), coeffs, rounds)) @ Vt
+
+
+@pytest.mark.parametrize("shape", [(24, 80), (80, 24)])
+@pytest.mark.parametrize("mode", ["plain", "gram"])
+def test_orthogonalise_full_rank_closed_form(shape, mode):
+    """Full rank with a spread spectrum (spectral norm well below the Frobenius norm), so any
+    other normalisation changes every output singular value."""
+    rng = np.random.default_rng(31)
+    m, n = shape
+    k = min(m, n)
+    U, _ = np.linalg.qr(rng.standard_normal((m, k)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    G = (U * np.geomspace(7.0, 0.05, k)) @ V.T
+    O = om.orthogonalise(G, eps=0.0, mode=mode)
+    assert O.shape == G.shape
+    assert rel(O, normalised_closed_form(G, COEFFS, 5)) < 1e-12
+
+
+@pytest.mark.parametrize("kind", ["spectral", "eps_in_square", "none", "max_abs"])
+def test_planted_normalisation_mistakes_are_caught(kind, monkeypatch):
+    slips = {
+        "spectral": lambda X, eps: om.as_f64(X) / (np.linalg.norm(om.as_f64(X), 2) + eps),
+        "eps_in_square": lambda X, eps: om.as_f64(X) / np.sqrt(np.sum(om.as_f64(X) ** 2) + eps),
+        "none": lambda X, eps: om.as_f64(X),
+        "max_abs": lambda X, eps: om.as_f64(X) / (np.max(np.abs(om.as_f64(X))) + eps),
+    }
+    monkeypatch.setattr(om, "frobenius_normalise", slips[kind])
+    failures = 0
+    checks = [test_frobenius_normalise_rank_two] + [
+        (lambda mode=mode: test_orthogonalise_full_rank_closed_form((24, 80), mode)) for mode in ("plain", "gram")]
+    for check in checks:
+        try:
+            check()
+        except AssertionError:
+            failures += 1
+    assert failures > 0, kind

@@ -197,7 +197,7 @@ def main():
                         w_dtype=w.w_dtype, g_dtype=w.g_dtype, m_dtype=w.m_dtype, ns_dtype=w.ns_dtype)
     ctx = B.muon_init(0)
     pctx = B.muon_init(0, B.MUON_FLAG_PROFILE)
-    arr = B.matrix_list(mats)
+    arr = B.matrix_list(mats, hp, 0)
     nbytes = B.muon_workspace_size(ctx, mats, hp)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()

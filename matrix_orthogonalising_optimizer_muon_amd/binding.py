@@ -174,18 +174,47 @@ def make_hparams(*, lr=None, momentum=None, weight_decay=None, eps=None, nestero
     return hp
 
 
-def matrix_list(mats) -> ctypes.Array:
+TORCH_DTYPES = {MUON_F32: torch.float32, MUON_BF16: torch.bfloat16}
+
+
+def _check_dtype(x, name: str, dtype_code: int | None) -> None:
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(x).__name__}")
+    if dtype_code is not None and x.dtype != TORCH_DTYPES[dtype_code]:
+        raise TypeError(f"{name} has dtype {x.dtype}, the hyper-parameters say {TORCH_DTYPES[dtype_code]}")
+
+
+def _check_device_tensor(x, name: str, dtype_code: int | None, device: int | None) -> None:
+    """A tensor handed to the library as a device pointer: contiguous, on a GPU (the
+    context's device when given) and in the storage dtype the hyper-parameters name."""
+    _check_dtype(x, name, dtype_code)
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} is on {x.device}, not on a GPU")
+    if device is not None and x.device.index != device:
+        raise ValueError(f"{name} is on {x.device}, the context is on cuda:{device}")
+
+
+def matrix_list(mats, hp: muon_hparams | None = None, device: int | None = None) -> ctypes.Array:
     """Build a ``muon_matrix[]`` from (W, G, M) torch tensors or (W, G, M, rows, cols)
-    tuples of raw pointers."""
+    tuples of raw pointers. Tensors must be 2-D, contiguous, of one shape and on a GPU
+    (``device`` when given); with ``hp`` their dtypes must be ``hp``'s w/g/m dtypes."""
     arr = (muon_matrix * max(1, len(mats)))()
     for i, t in enumerate(mats):
         if len(t) == 3:
             W, G, M = t
-            for x in (W, G, M):
-                if x.dim() != 2 or not x.is_contiguous():
-                    raise ValueError("W, G, M must be contiguous 2-D tensors")
+            codes = (hp.w_dtype, hp.g_dtype, hp.m_dtype) if hp is not None else (None, None, None)
+            for x, name, code in zip((W, G, M), ("W", "G", "M"), codes):
+                _check_dtype(x, f"matrix {i} {name}", code)
+            for x, name, code in zip((W, G, M), ("W", "G", "M"), codes):
+                _check_device_tensor(x, f"matrix {i} {name}", code, device)
+                if x.dim() != 2:
+                    raise ValueError(f"matrix {i} {name} must be 2-D")
             if not (W.shape == G.shape == M.shape):
-                raise ValueError("W, G, M shapes differ")
+                raise ValueError(f"matrix {i}: W, G, M shapes differ")
+            if len({W.device, G.device, M.device}) != 1:
+                raise ValueError(f"matrix {i}: W, G, M on different devices")
             arr[i] = muon_matrix(W.data_ptr(), G.data_ptr(), M.data_ptr(), W.shape[0], W.shape[1])
         else:
             W, G, M, r, c = t
@@ -211,7 +240,7 @@ def muon_workspace_size(ctx, mats, hp: muon_hparams) -> int:
 def muon_step(ctx, mats, hp: muon_hparams, workspace_ptr: int, workspace_bytes: int,
               stream_ptr: int | None = None, count: int | None = None) -> int:
     """Enqueue one update; returns the status (use ``check`` to raise)."""
-    arr = mats if isinstance(mats, ctypes.Array) else matrix_list(mats)
+    arr = mats if isinstance(mats, ctypes.Array) else matrix_list(mats, hp)
     n = len(mats) if count is None else count
     if stream_ptr is None:
         stream_ptr = torch.cuda.current_stream().cuda_stream
@@ -268,21 +297,34 @@ def make_adamw_hparams(**kw) -> muon_adamw_hparams:
     return hp
 
 
-def adamw_tensor_list(tensors) -> ctypes.Array:
+def adamw_tensor_list(tensors, hp: muon_adamw_hparams | None = None, device: int | None = None) -> ctypes.Array:
     """Build a ``muon_adamw_tensor[]`` from (W, G, m, v) torch tensors (numel from W) or from
-    (W, G, m, v, numel) raw pointer tuples."""
+    (W, G, m, v, numel) raw pointer tuples. Tensors must be contiguous, on a GPU (``device``
+    when given) and of one element count; m and v are fp32, and with ``hp`` W and G must be
+    in its w/g dtypes."""
     arr = (muon_adamw_tensor * max(len(tensors), 1))()
     for i, t in enumerate(tensors):
         if len(t) == 5:
             arr[i] = muon_adamw_tensor(t[0], t[1], t[2], t[3], int(t[4]))
         else:
             W, G, m, v = t
+            codes = (hp.w_dtype, hp.g_dtype) if hp is not None else (None, None)
+            for x, name, code in ((W, "W", codes[0]), (G, "G", codes[1]), (m, "m", MUON_F32), (v, "v", MUON_F32)):
+                _check_dtype(x, f"tensor {i} {name}", code)
+            _check_device_tensor(W, f"tensor {i} W", codes[0], device)
+            _check_device_tensor(G, f"tensor {i} G", codes[1], device)
+            _check_device_tensor(m, f"tensor {i} m", MUON_F32, device)
+            _check_device_tensor(v, f"tensor {i} v", MUON_F32, device)
+            if not (W.numel() == G.numel() == m.numel() == v.numel()):
+                raise ValueError(f"tensor {i}: W, G, m, v element counts differ")
+            if len({W.device, G.device, m.device, v.device}) != 1:
+                raise ValueError(f"tensor {i}: W, G, m, v on different devices")
             arr[i] = muon_adamw_tensor(W.data_ptr(), G.data_ptr(), m.data_ptr(), v.data_ptr(), W.numel())
     return arr
 
 
 def muon_adamw_step(ctx, tensors, hp: muon_adamw_hparams, stream_ptr=None, count=None) -> int:
-    arr = tensors if isinstance(tensors, ctypes.Array) else adamw_tensor_list(tensors)
+    arr = tensors if isinstance(tensors, ctypes.Array) else adamw_tensor_list(tensors, hp)
     n = len(tensors) if count is None else count
     if stream_ptr is None:
         stream_ptr = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None

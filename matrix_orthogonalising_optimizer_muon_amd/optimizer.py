@@ -20,12 +20,26 @@ from . import binding as B
 
 class MuonUpdate:
     def __init__(self, mats, device: int | None = None, **hparams):
-        self.device = torch.cuda.current_device() if device is None else int(device)
-        self.ctx = B.muon_init(self.device)
-        self.hp = B.make_hparams(**hparams)
         self.tensors = list(mats)
+        if device is None:
+            device = self.tensors[0][0].device.index if self.tensors else torch.cuda.current_device()
+        self.device = int(device)
+        # Storage dtypes come from the tensors (every W alike, every G alike, every M alike);
+        # a dtype also given by keyword must agree with them.
+        for role, k in (("w_dtype", 0), ("g_dtype", 1), ("m_dtype", 2)):
+            names = {_dtype_name(t[k].dtype) for t in self.tensors}
+            if len(names) > 1:
+                raise TypeError(f"mixed {role[0].upper()} dtypes {sorted(names)}: use one MuonUpdate per dtype")
+            if names:
+                got = names.pop()
+                if hparams.get(role) not in (None, got):
+                    raise TypeError(f"{role}={hparams[role]!r} but the tensors are {got}")
+                hparams[role] = got
+        self.hp = B.make_hparams(**hparams)
         self.count = len(self.tensors)
-        self.arr = B.matrix_list(self.tensors)
+        # validates device, contiguity, shapes and dtypes before the context is created
+        self.arr = B.matrix_list(self.tensors, self.hp, self.device)
+        self.ctx = B.muon_init(self.device)
         nbytes = B.muon_workspace_size(self.ctx, self.tensors, self.hp)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8,
                                      device=f"cuda:{self.device}")
@@ -40,7 +54,7 @@ class MuonUpdate:
         return B.muon_plan_info(self.ctx, self.tensors, self.hp, index)
 
     def close(self) -> None:
-        if self.ctx is not None:
+        if getattr(self, "ctx", None) is not None:
             B.muon_destroy(self.ctx)
             self.ctx = None
 

@@ -391,3 +391,49 @@ def test_auto_schedule_workspace_covers_both_forms(hctx):
             B.muon_workspace_size(mctx, [(0, 0, 0, 2048, 2048)], B.make_hparams(mode="gram"))
     finally:
         B.muon_destroy(mctx)
+
+
+def test_binding_rejects_bad_tensors():
+    """The binding hands tensors over as device pointers only when they are contiguous, on
+    a GPU and in the hyper-parameters' storage dtypes; everything else raises before the
+    library is called (checked here with host tensors, which can never be passed)."""
+    import torch
+    hp = B.make_hparams(w_dtype="f32", g_dtype="bf16", m_dtype="bf16")
+    W = torch.zeros(4, 8)
+    G = torch.zeros(4, 8, dtype=torch.bfloat16)
+    M = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        B.matrix_list([(W, G, M)], hp)
+    with pytest.raises(TypeError, match="dtype"):
+        B.matrix_list([(W.to(torch.bfloat16), G, M)], hp)       # bf16 W where hp says f32
+    with pytest.raises(TypeError, match="dtype"):
+        B.matrix_list([(W, G.float(), M)], hp)
+    with pytest.raises(ValueError, match="contiguous"):
+        B.matrix_list([(torch.zeros(8, 4).t(), G, M)], hp)
+    with pytest.raises(TypeError):
+        B.matrix_list([(W, G, "M")], hp)
+    ahp = B.make_adamw_hparams(w_dtype="f32", g_dtype="bf16")
+    n = 16
+    good = (torch.zeros(n), torch.zeros(n, dtype=torch.bfloat16), torch.zeros(n), torch.zeros(n))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        B.adamw_tensor_list([good], ahp)
+    with pytest.raises(TypeError, match="dtype"):
+        B.adamw_tensor_list([(good[0], good[1], good[2].double(), good[3])], ahp)
+    with pytest.raises(TypeError, match="dtype"):
+        B.adamw_tensor_list([(good[0].to(torch.bfloat16),) + good[1:]], ahp)
+
+
+def test_muon_update_takes_dtypes_from_tensors():
+    """MuonUpdate reads the storage dtypes off the tensors and rejects a conflicting keyword
+    or a mixed list before any device work."""
+    import torch
+    from matrix_orthogonalising_optimizer_muon_amd.optimizer import MuonUpdate
+    W = torch.zeros(4, 8, dtype=torch.bfloat16)
+    G = torch.zeros(4, 8, dtype=torch.bfloat16)
+    M = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="w_dtype"):
+        MuonUpdate([(W, G, M)], device=0, w_dtype="f32")
+    with pytest.raises(TypeError, match="mixed"):
+        MuonUpdate([(W, G, M), (W.float(), G, M)], device=0)
+    with pytest.raises(ValueError, match="not on a GPU"):    # dtypes agree; host tensors
+        MuonUpdate([(W, G, M)], device=0)

@@ -48,7 +48,7 @@ class FullRun:
         self.reset()
         self.G = [wl.gradient_torch(w, 0, i) for i in range(len(w.matrices))]
         mats = list(zip(self.W, self.G, self.M))
-        self.arr = B.matrix_list(mats)
+        self.arr = B.matrix_list(mats, self.hp, 0)
         self.nbytes = B.muon_workspace_size(self.ctx, mats, self.hp)
         self.ws = torch.empty(self.nbytes, dtype=torch.uint8, device="cuda")
         self.step()            # measures every stage's tiles (as bench.py's warm-up does)

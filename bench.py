@@ -27,7 +27,8 @@ if ROOT not in sys.path:
 
 PEAK = {"bf16": 2500.0, "f32": 157.3}       # dense MFMA TFLOP/s (MI355X public figures)
 HBM_PEAK_GBS = 8000.0
-GEMM_STAGES = ("syrk_u", "syrk", "square", "apply", "apply_update")
+GEMM_STAGES = ("syrk", "square", "apply", "apply_update")
+HBM_STAGES = ("momentum_norm", "norm_finalize", "momentum")
 
 
 def parse():
@@ -35,7 +36,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="single_bf16_2560x9728")
+    ap.add_argument("--workload", default="dense_7b_28layers",
+                    help="the 196-matrix 7B shape set (the largest workload, the default), or any "
+                         "other workload of matrix_orthogonalising_optimizer_muon_amd.workloads")
+    ap.add_argument("--also", default="single_bf16_2560x9728",
+                    help="comma-separated further workloads timed in the same run (reported under "
+                         "\"also\": ms per step, GEMM rate, dominant kernel); empty for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--details", action="store_true", help="also print the per-stage table to stderr")
@@ -109,7 +115,30 @@ def cpu_baseline(w, budget_s):
               f"{t_used:.1f} s)" + ("" if n_done == len(w.matrices) else
                                     f"; scaled x{scale:.2f} by model FLOPs to the whole list"))
     return {"value": round(t_used * scale * 1e3, 3), "unit": "ms", "cores": cores, "kind": "oracle",
-            "sample": sample}
+            "sample": sample, "cpu": cpu_model(), "blas": blas_vendor()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_vendor():
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '')}, "
+                f"{i.get('num_threads')} threads)" for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            return "; ".join(libs)
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 TRAFFIC_SOURCES = ("matrix_orthogonalising_optimizer_muon_amd/csrc/gemm.hip",
@@ -176,27 +205,21 @@ def adamw_bench(B, ctx, torch, args):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "exchange of the update is not built here", file=sys.stderr)
-        sys.exit(2)
+NS_DESC = {"auto": "auto: plain NS (5 rounds) or Gram NS 2+2+1 per shape, by measured stage cost",
+           "gram": "Gram 2+2+1", "plain": "plain 5 rounds",
+           "auto_schedule": "auto_schedule: plain NS or Gram NS with k balanced segments (5 rounds), "
+                            "per shape by measured stage cost"}
 
-    import torch
-    from matrix_orthogonalising_optimizer_muon_amd import binding as B
-    from matrix_orthogonalising_optimizer_muon_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
-    torch.cuda.set_device(0)
+def run_workload(w, args, B, torch, ctx, pctx, primary):
+    """Inputs resident in HBM, warm-up (measures the tiles), K event-timed steps, then K
+    steps with per-launch events for the stage table. Frees its buffers on return."""
     print(f"[bench] workload {w.name}: {len(w.matrices)} matrices, {w.elements / 1e6:.1f} M elements",
           file=sys.stderr, flush=True)
     Ws, Gs, Ms, data = make_inputs(w, torch)
     mats = list(zip(Ws, Gs, Ms))
     hp = B.make_hparams(lr=w.lr, momentum=w.mu, weight_decay=w.wd, mode=args.mode,
                         w_dtype=w.w_dtype, g_dtype=w.g_dtype, m_dtype=w.m_dtype, ns_dtype=w.ns_dtype)
-    ctx = B.muon_init(0)
-    pctx = B.muon_init(0, B.MUON_FLAG_PROFILE)
     arr = B.matrix_list(mats, hp, 0)
     nbytes = B.muon_workspace_size(ctx, mats, hp)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -206,7 +229,7 @@ def main():
     def step(c):
         B.check(B.muon_step(c, arr, hp, ws.data_ptr(), nbytes, sp, count=len(mats)), "muon_step")
 
-    if args.calibrate_copy_mib > 0:
+    if primary and args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * 1024 * 1024 // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -217,13 +240,13 @@ def main():
               flush=True)
         del src, dst
 
-    if args.tune_cache and os.path.exists(args.tune_cache):
+    if primary and args.tune_cache and os.path.exists(args.tune_cache):
         n = B.muon_tune_load(ctx, args.tune_cache)
         print(f"[bench] {n} tile choices loaded from {args.tune_cache}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step(ctx)
     torch.cuda.synchronize()
-    if args.tune_cache:
+    if primary and args.tune_cache:
         B.muon_tune_save(ctx, args.tune_cache)
     print(f"[bench] warmup done ({args.warmup} steps), workspace {nbytes / 2**30:.2f} GiB",
           file=sys.stderr, flush=True)
@@ -264,7 +287,7 @@ def main():
     edges = [e0] + marks + [e1]
     per_step = sorted(edges[i].elapsed_time(edges[i + 1]) for i in range(args.steps))
     pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
-    print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
+    print(f"[bench] {w.name}: timed {args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
           file=sys.stderr, flush=True)
 
     # Second pass with per-launch events (library profiler) for the per-kernel roofline.
@@ -275,6 +298,23 @@ def main():
         step(pctx)
     torch.cuda.synchronize()
     prof = B.muon_profile_read(pctx, 4096)
+    plans = {}
+    for i, spec in enumerate(w.matrices):
+        key = f"{min(spec.rows, spec.cols)}x{max(spec.rows, spec.cols)}"
+        if key in plans:
+            continue
+        e = B.muon_plan_info(ctx, mats, hp, i)
+        plans[key] = {"mode": {1: "plain", 2: "gram"}[e.mode], "tile_sym": e.tile_sym,
+                      "tile_apply": e.tile_apply, "segments": list(e.segments[:e.n_segments])}
+    del Ws, Gs, Ms, mats, arr, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"ms": ms, "pct": (pct(0.1), pct(0.5), pct(0.9)), "prof": prof, "plans": plans, "data": data}
+
+
+def summarise(w, r, args):
+    """Dominant GEMM kernel, GEMM and HBM-phase rates and the stage table of a run."""
+    prof = r["prof"]
     gemm = [e for e in prof if e["stage"] in GEMM_STAGES]
     dom = max(gemm, key=lambda e: e["total_ms"])
     avg_ms = dom["total_ms"] / dom["launches"]
@@ -283,38 +323,18 @@ def main():
     peak = PEAK[w.ns_dtype]
     gemm_flops = sum(e["flops"] for e in gemm) / args.steps
     gemm_ms = sum(e["total_ms"] for e in gemm) / args.steps
+    hbm = [e for e in prof if e["stage"] in HBM_STAGES]
+    hbm_gbs = (sum(e["bytes"] for e in hbm) / (sum(e["total_ms"] for e in hbm) * 1e-3) / 1e9) if hbm else None
     mom = [e for e in prof if e["stage"] == "momentum"]
     mom_gbs = (sum(e["bytes"] for e in mom) / (sum(e["total_ms"] for e in mom) * 1e-3) / 1e9) if mom else None
-    prof_ms = sum(e["total_ms"] for e in prof) / args.steps
     if args.details:
         for e in prof:
             rate = (e["flops"] / (e["total_ms"] * 1e-3) / 1e12) if e["flops"] else 0.0
-            print(f"[stage] {e['stage']:14s} m'={e['m']:6d} n'={e['n']:6d} x{e['count']:4d} "
+            print(f"[stage] {w.name} {e['stage']:14s} m'={e['m']:6d} n'={e['n']:6d} x{e['count']:4d} "
                   f"launches={e['launches']:5d} avg={e['total_ms'] / e['launches'] * 1e3:9.2f} us "
                   f"{rate:8.1f} TFLOP/s", file=sys.stderr)
-
-    out = {
-        "metric": "Muon optimizer-step ms per shape set; GEMM TFLOP/s as % of bf16 MFMA peak",
-        "value": round(ms, 4),
-        "unit": "ms",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.ns_dtype == "bf16" else "f32",
-        "data": f"synthetic ({data})",
-        "config": {"workload": w.name, "matrices": len(w.matrices), "elements": w.elements,
-                   "launch": "hip graph replay" if args.graph else "eager",
-                   "shapes": sorted({f"{s.rows}x{s.cols}" for s in w.matrices}),
-                   "ns": {"auto": "auto (FLOP-model dispatch: Gram 2+2+1 or plain 5 rounds)",
-                          "gram": "Gram 2+2+1", "plain": "plain 5 rounds",
-                          "auto_schedule": "auto_schedule (plain or Gram with k balanced segments, "
-                                           "5 rounds, per shape by measured stage times)"}[args.mode],
-                   "storage": {"W": w.w_dtype, "G": w.g_dtype, "M": w.m_dtype}},
+    return {
+        "dom": dom,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": None,
                      "kernel": f"{dom['stage']} m'={dom['m']} n'={dom['n']} x{dom['count']} tile {dom['tile']}",
@@ -324,7 +344,9 @@ def main():
         "gemm_frac_of_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak, 4),
         "momentum_gbs": None if mom_gbs is None else round(mom_gbs, 1),
         "momentum_frac_of_hbm": None if mom_gbs is None else round(mom_gbs / HBM_PEAK_GBS, 4),
-        "profiled_ms_per_step": round(prof_ms, 4),
+        "hbm_phase_gbs": None if hbm_gbs is None else round(hbm_gbs, 1),
+        "hbm_phase_frac_of_hbm": None if hbm_gbs is None else round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "profiled_ms_per_step": round(sum(e["total_ms"] for e in prof) / args.steps, 4),
         # per stage and shape group, from the profiled pass: launches per step, average
         # launch time (us, hipEvents on the launch stream), achieved TFLOP/s or GB/s
         "stages": [{"stage": e["stage"], "group": f"{e['m']}x{e['n']}x{e['count']}", "tile": e["tile"],
@@ -335,18 +357,52 @@ def main():
                        if e["bytes"] and not e["flops"] else {})}
                    for e in prof],
     }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
-    plans = {}
-    for i, spec in enumerate(w.matrices):
-        key = f"{min(spec.rows, spec.cols)}x{max(spec.rows, spec.cols)}"
-        if key in plans:
-            continue
-        e = B.muon_plan_info(ctx, mats, hp, i)
-        plans[key] = {"mode": {1: "plain", 2: "gram"}[e.mode], "tile_sym": e.tile_sym,
-                      "tile_apply": e.tile_apply, "segments": list(e.segments[:e.n_segments])}
-    out["config"]["plan"] = plans
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "exchange of the update is not built here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from matrix_orthogonalising_optimizer_muon_amd import binding as B
+    from matrix_orthogonalising_optimizer_muon_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    ctx = B.muon_init(0)
+    pctx = B.muon_init(0, B.MUON_FLAG_PROFILE)
+    r = run_workload(w, args, B, torch, ctx, pctx, primary=True)
+    sm = summarise(w, r, args)
+    ms = r["ms"]
+    dom = sm.pop("dom")
+    out = {
+        "metric": "Muon optimizer-step ms per shape set; GEMM TFLOP/s as % of bf16 MFMA peak",
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "step_ms_p10_p50_p90": [round(x, 4) for x in r["pct"]],
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.ns_dtype == "bf16" else "f32",
+        "data": f"synthetic ({r['data']})",
+        "config": {"workload": w.name, "matrices": len(w.matrices), "elements": w.elements,
+                   "launch": "hip graph replay" if args.graph else "eager",
+                   "shapes": sorted({f"{s.rows}x{s.cols}" for s in w.matrices}),
+                   "ns": NS_DESC[args.mode],
+                   "precision": ("G, M bf16 storage; W fp32; NS iterate and m'xm' recurrence in fp16 "
+                                 "(power-of-two prescaled) on fp16 MFMA with fp32 accumulation"
+                                 if w.ns_dtype == "bf16" else "fp32 throughout (fp32 MFMA)"),
+                   "storage": {"W": w.w_dtype, "G": w.g_dtype, "M": w.m_dtype},
+                   "plan": r["plans"]},
+        **sm,
+    }
     rec = traffic_record(w.name)
     st = rec["kernels"].get(f"{dom['stage']}/{dom['tile']}") if rec else None
     if st is not None:
@@ -355,6 +411,23 @@ def main():
         out["roofline"]["traffic_kernel"] = st["kernel"]
         if "trace_avg_us" in st:
             out["roofline"]["rocprof_avg_us"] = st["trace_avg_us"]
+    also = [x for x in args.also.split(",") if x and x != w.name] if args.also else []
+    if also:
+        out["also"] = {}
+        for name in also:
+            wa = wl.WORKLOADS[name]
+            ra = run_workload(wa, args, B, torch, ctx, pctx, primary=False)
+            sa = summarise(wa, ra, args)
+            sa.pop("dom")
+            out["also"][name] = {"ms_per_step": round(ra["ms"], 4),
+                                 "step_ms_p10_p50_p90": [round(x, 4) for x in ra["pct"]],
+                                 "plan": ra["plans"],
+                                 **{k: sa[k] for k in ("roofline", "gemm_tflops", "gemm_frac_of_peak",
+                                                       "momentum_gbs", "hbm_phase_gbs", "profiled_ms_per_step",
+                                                       "stages")}}
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
     if args.adamw:
         out["adamw_companion"] = adamw_bench(B, ctx, torch, args)
     B.muon_destroy(ctx)

@@ -45,7 +45,9 @@ extern "C" {
 #define MUON_BF16 1
 
 /* ---- Newton-Schulz form ---- */
-#define MUON_NS_AUTO 0   /* per shape: the dispatcher picks plain or Gram */
+#define MUON_NS_AUTO 0   /* per shape: the dispatcher picks plain or Gram (with the given
+                            segments) by cost: the shape's measured stage times once its tiles
+                            are measured, else the MuonX article's dense FLOP count */
 #define MUON_NS_PLAIN 1  /* sum(segments) plain rounds (segments ignored otherwise) */
 #define MUON_NS_GRAM 2   /* Gram-space NS with the given segments */
 #define MUON_NS_AUTO_SCHEDULE 3  /* per shape: plain NS or Gram NS with k segments, chosen below */
@@ -137,9 +139,10 @@ typedef struct muon_plan_entry {
 
 /* Aggregated launch timings of one stage kind, shape and tile (muon_profile_read). */
 typedef struct muon_profile_entry {
-  char stage[32];        /* "table", "momentum", "norm_finalize", "transpose", "syrk_u"
-                            (Gram product of the momentum output), "syrk" (of the
-                            iterate), "square", "apply", "apply_update" */
+  char stage[32];        /* "table", "momentum_norm" (first pass over G and M: the partial
+                            sums of U^2), "norm_finalize", "momentum" (second pass: M' and
+                            the normalised iterate in both layouts), "syrk" (Gram product of
+                            the iterate), "square", "apply", "apply_update", "single_wg" */
   int64_t m, n;          /* canonical shape of the group the launches served */
   int32_t count;         /* matrices per launch */
   int32_t launches;      /* launches aggregated */
@@ -195,14 +198,17 @@ int muon_step(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hpar
 /* Measured tile choices, shared by every context of the process, to and from a text file,
  * so that another process starts with the same choices instead of measuring again
  * (DMuon summary, section 2.4: per-shape configurations measured once and cached). One
- * choice per line: "stage path padded_m padded_n batch tile" (stage: 0 Gram product of
- * the momentum output, 1 m' x m' product, 2 apply, 4 Gram product of the iterate; path:
- * 0 bf16, 1 fp32; tile: as in muon_debug_gemm). muon_tune_save writes the choices made on
- * the context's device (overwriting the file). muon_tune_load validates the whole file
- * first and then adds its choices for the context's device, replacing choices already
- * held for the same key; *n_loaded (may be null) receives their number. A missing or
- * unreadable file, a malformed line or a tile unavailable for its stage returns
- * MUON_ERR_ARG and changes nothing. Host-only contexts save and load too. */
+ * choice per line: "stage path padded_m padded_n batch tile ms" (stage: 1 m' x m'
+ * product, 2 apply, 4 Gram product of the iterate (0 is the bf16 Gram product that only
+ * muon_debug_gemm runs); path: 0 bf16, 1 fp32; tile: as in muon_debug_gemm; ms: the
+ * measured time of one launch with that tile, which MUON_NS_AUTO and
+ * MUON_NS_AUTO_SCHEDULE use as the stage's cost, negative or absent when unknown).
+ * muon_tune_save writes the choices made on the context's device (overwriting the file).
+ * muon_tune_load validates the whole file first and then adds its choices for the
+ * context's device, replacing choices already held for the same key; *n_loaded (may be
+ * null) receives their number. A missing or unreadable file, a malformed line or a tile
+ * unavailable for its stage returns MUON_ERR_ARG and changes nothing. Host-only contexts
+ * save and load too. */
 int muon_tune_save(muon_ctx *ctx, const char *path);
 int muon_tune_load(muon_ctx *ctx, const char *path, int *n_loaded);
 

@@ -79,11 +79,12 @@ struct Group {
   std::vector<int> members;    // indices into the caller's list
   int table_base = 0;          // first descriptor of this group in the table
   // workspace offsets (bytes) and per-matrix element strides
-  // X: canonical m' x n' iterate (first the momentum output U); XT[2]: its transposed
+  // X: canonical m' x n' iterate (first X0 = xs s U); XT[2]: its transposed
   // copies (ping-pong); SQ: m' x m' buffers of the Gram-space recurrence.
   size_t off_partials = 0, off_s = 0, off_x = 0, off_xt[2] = {0, 0}, off_sq[4] = {0, 0, 0, 0};
   int64_t stride_x = 0, stride_sq = 0;
   int mom_tiles_m = 0, mom_tiles_n = 0;
+  int norm_blocks = 0;         // 4096-element blocks of one stored matrix (norm partials)
   bool single_wg = false;      // whole update per matrix in one workgroup (small shapes)
   bool has_tall = false;       // some member is stored transposed (rows > cols)
   double work = 0.0;
@@ -158,12 +159,28 @@ double kernel_flops(int64_t m, int64_t n, int mode, const muon_hparams& hp) {
   return f;
 }
 
-// Shape-adaptive choice of the NS form: Gram pays when the long products it saves cost
-// more than the square ones it adds (MuonX section 3.2: benefit depends on the shape).
-int choose_mode(int64_t m, int64_t n, const muon_hparams& hp) {
+// Per-product costs of a group's shape: the measured times of its Gram product, m' x m'
+// product and apply once a step has measured their tiles (and the context measures),
+// else the FLOPs the kernels perform (m'^2 n', m'^3 and 2 m'^2 n'). Returns true when the
+// costs are measured.
+bool product_costs(const muon_ctx* ctx, const Group& g, bool f32, double& ts, double& tq, double& ta);
+
+// Shape-adaptive choice of the NS form for MUON_NS_AUTO: Gram NS with the caller's
+// segments pays when the long products it saves cost more than the square ones it adds
+// (MuonX section 3.2: the benefit depends on the shape). The costs are the shape's
+// measured stage times once its tiles are measured, before that the dense FLOP counts
+// the article uses (plain r (2L + S) against Gram sum_j (2L + (4 s_j - 3) S)).
+int choose_mode(const muon_ctx* ctx, const Group& g, const muon_hparams& hp, bool f32) {
   if (hp.mode != MUON_NS_AUTO) return hp.mode;  // AUTO_SCHEDULE is resolved per group later
-  return dense_flops(m, n, MUON_NS_GRAM, hp) < dense_flops(m, n, MUON_NS_PLAIN, hp) ? MUON_NS_GRAM
-                                                                                      : MUON_NS_PLAIN;
+  double ts, tq, ta;
+  if (product_costs(ctx, g, f32, ts, tq, ta)) {
+    const int R = total_rounds(hp);
+    double gram = 0.0;
+    for (int i = 0; i < hp.n_segments; ++i) gram += ts + ta + (4.0 * hp.segments[i] - 3.0) * tq;
+    return gram < R * (ts + tq + ta) ? MUON_NS_GRAM : MUON_NS_PLAIN;
+  }
+  return dense_flops(g.m, g.n, MUON_NS_GRAM, hp) < dense_flops(g.m, g.n, MUON_NS_PLAIN, hp) ? MUON_NS_GRAM
+                                                                                          : MUON_NS_PLAIN;
 }
 
 // Static tile choice (MUON_FLAG_MODEL_ONLY, and the default before a measurement):
@@ -217,7 +234,7 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
       const int64_t cnt = static_cast<int64_t>(g.members.size());
       g.hs = hp;
       if (hp.mode == MUON_NS_AUTO_SCHEDULE) choose_schedule(ctx, g, hp, f32);
-      else g.mode = choose_mode(m, n, hp);
+      else g.mode = choose_mode(ctx, g, hp, f32);
       g.hs.mode = g.mode;
       g.tile_sq = heuristic_sym(g.Mp, cnt, ctx->cu_count);
       g.tile_ap = heuristic_apply(g.Mp, g.Np, cnt, ctx->cu_count, f32);
@@ -250,7 +267,8 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
     g.mom_tiles_m = static_cast<int>(g.Mp / 64);
     g.mom_tiles_n = static_cast<int>(g.Np / 64);
     g.off_partials = off;
-    off = align_up(off + sizeof(float) * cnt * g.mom_tiles_m * g.mom_tiles_n);
+    g.norm_blocks = static_cast<int>((g.m * g.n + kNormBlock - 1) / kNormBlock);
+    off = align_up(off + sizeof(float) * cnt * g.norm_blocks);
     g.off_s = off;
     off = align_up(off + sizeof(float) * cnt);
     g.stride_x = g.Mp * g.Np;
@@ -261,10 +279,10 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
       off = align_up(off + ex * static_cast<size_t>(g.stride_x) * cnt);
     }
     g.stride_sq = g.Mp * g.Mp;
-    // The automatic schedule may pick plain NS before a shape's tiles are measured and
-    // Gram NS after, so it always reserves the Gram path's four m' x m' buffers: the
+    // The automatic choices may pick plain NS before a shape's tiles are measured and
+    // Gram NS after, so they always reserve the Gram path's four m' x m' buffers: the
     // workspace size does not change between steps.
-    const int nsq = (g.mode == MUON_NS_GRAM || hp.mode == MUON_NS_AUTO_SCHEDULE) ? 4 : 2;
+    const int nsq = (g.mode == MUON_NS_GRAM || hp.mode == MUON_NS_AUTO || hp.mode == MUON_NS_AUTO_SCHEDULE) ? 4 : 2;
     for (int k = 0; k < nsq; ++k) {
       g.off_sq[k] = off;
       off = align_up(off + esq * static_cast<size_t>(g.stride_sq) * cnt);
@@ -283,12 +301,12 @@ struct StepEnv {
   muon_ctx* ctx;
 };
 
-// One stage name per kernel symbol: "syrk_u" is the Gram product of the momentum output
-// (bf16 operands on the bf16 path), "syrk" the one of the fp16 / fp32 iterate.
-constexpr const char* kStageNames[] = {"table", "momentum", "norm_finalize", "transpose", "syrk",
-                                       "square", "apply", "apply_update", "syrk_u", "single_wg"};
-enum Stage { ST_TABLE, ST_MOMENTUM, ST_FINALIZE, ST_TRANSPOSE, ST_SYRK, ST_SQUARE, ST_APPLY, ST_UPDATE,
-             ST_SYRK_U, ST_SINGLE_WG };
+// One stage name per kernel: "momentum_norm" the first pass over G and M (partial sums of
+// U^2), "momentum" the second (M' and the normalised iterate in both layouts).
+constexpr const char* kStageNames[] = {"table", "momentum", "norm_finalize", "momentum_norm", "syrk",
+                                       "square", "apply", "apply_update", "single_wg"};
+enum Stage { ST_TABLE, ST_MOMENTUM, ST_FINALIZE, ST_MOMENTUM_NORM, ST_SYRK, ST_SQUARE, ST_APPLY, ST_UPDATE,
+             ST_SINGLE_WG };
 constexpr size_t kMaxRecords = 1 << 16;
 
 // Brackets one launch with events when profiling is on (no effect otherwise).
@@ -362,20 +380,24 @@ std::map<TuneKey, float> g_tuned_ms;   // measured time of the chosen configurat
 // shape's Gram product, m' x m' product and apply when a step has measured their tiles,
 // else the FLOPs the kernels perform (m'^2 n', m'^3 and 2 m'^2 n'). Ties keep plain NS,
 // then the larger k.
+bool product_costs(const muon_ctx* ctx, const Group& g, bool f32, double& ts, double& tq, double& ta) {
+  ts = 1.0 * g.m * g.m * g.n; ta = 2.0 * g.m * g.m * g.n; tq = 1.0 * g.m * g.m * g.m;
+  if (ctx->flags & MUON_FLAG_MODEL_ONLY) return false;
+  const int cnt = static_cast<int>(g.members.size());
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  auto s = g_tuned_ms.find(std::make_tuple(ctx->device, static_cast<int>(OP_SYRK), f32 ? 1 : 0, g.Mp, g.Mp, cnt));
+  auto q = g_tuned_ms.find(std::make_tuple(ctx->device, static_cast<int>(OP_SYM), f32 ? 1 : 0, g.Mp, g.Mp, cnt));
+  auto a = g_tuned_ms.find(std::make_tuple(ctx->device, static_cast<int>(OP_APPLY), f32 ? 1 : 0, g.Mp, g.Np, cnt));
+  if (s == g_tuned_ms.end() || q == g_tuned_ms.end() || a == g_tuned_ms.end()) return false;
+  ts = s->second; tq = q->second; ta = a->second;
+  return true;
+}
+
 void choose_schedule(const muon_ctx* ctx, Group& g, const muon_hparams& hp, bool f32) {
   const int R = total_rounds(hp);
   const int cap = f32 ? kMaxRounds : kMaxBf16Segment;
-  double ts = 1.0 * g.m * g.m * g.n, ta = 2.0 * g.m * g.m * g.n, tq = 1.0 * g.m * g.m * g.m;
-  if (!(ctx->flags & MUON_FLAG_MODEL_ONLY)) {
-    const int cnt = static_cast<int>(g.members.size());
-    std::lock_guard<std::mutex> lk(g_tune_mu);
-    auto s = g_tuned_ms.find(std::make_tuple(ctx->device, static_cast<int>(OP_SYRK_IN), f32 ? 1 : 0, g.Mp, g.Mp, cnt));
-    auto q = g_tuned_ms.find(std::make_tuple(ctx->device, static_cast<int>(OP_SYM), f32 ? 1 : 0, g.Mp, g.Mp, cnt));
-    auto a = g_tuned_ms.find(std::make_tuple(ctx->device, static_cast<int>(OP_APPLY), f32 ? 1 : 0, g.Mp, g.Np, cnt));
-    if (s != g_tuned_ms.end() && q != g_tuned_ms.end() && a != g_tuned_ms.end()) {
-      ts = s->second; tq = q->second; ta = a->second;
-    }
-  }
+  double ts, tq, ta;
+  product_costs(ctx, g, f32, ts, tq, ta);
   double best = R * (ts + tq + ta);
   int best_k = 0;  // plain
   const int kmin = (R + cap - 1) / cap, kmax = std::min(R, MUON_MAX_SEGMENTS);
@@ -465,23 +487,21 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
   return launch_gemm(op, env.f32, cfg, p, env.st);
 }
 
-// R = alpha * X X^T (symmetric). `input`: X is the momentum output (bf16 kernels on the
-// bf16 path), else the fp16 / fp32 iterate.
-hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, float alpha, int spow,
-                bool input) {
+// R = alpha * X X^T (symmetric), X the fp16 / fp32 iterate.
+hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, float alpha) {
   auto build = [&](int cfg) {
     GemmParams p = base_params(g, env);
     p.A = X; p.B = X; p.C = R;
     p.lda = p.ldb = g.Np; p.ldc = g.Mp;
     p.sA = p.sB = g.stride_x; p.sC = g.stride_sq;
     p.M = p.N = static_cast<int32_t>(g.Mp); p.K = static_cast<int32_t>(g.Np);
-    p.alpha = alpha; p.alpha_spow = spow;
+    p.alpha = alpha;
     set_sym_tiles(p, g.Mp, cfg);
     return p;
   };
   const double cnt = static_cast<double>(g.members.size());
-  StageTimer tm(env.ctx, env.st, input ? ST_SYRK_U : ST_SYRK, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.n, 0.0);
-  const hipError_t e = run_stage(env, g, input ? OP_SYRK_IN : OP_SYRK, g.tile_sq, true, build, &tm.rec.tile);
+  StageTimer tm(env.ctx, env.st, ST_SYRK, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.n, 0.0);
+  const hipError_t e = run_stage(env, g, OP_SYRK, g.tile_sq, true, build, &tm.rec.tile);
   tm.done();
   return e;
 }
@@ -551,14 +571,11 @@ hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* 
 bool group_tuned(const muon_ctx* ctx, const Group& g, const muon_hparams& hp, bool f32) {
   if ((ctx->flags & MUON_FLAG_MODEL_ONLY) || g.single_wg) return true;
   (void)hp;
-  const int rounds = total_rounds(g.hs);
-  const bool more = (g.mode == MUON_NS_PLAIN) ? rounds > 1 : g.hs.n_segments > 1;
   const int cnt = static_cast<int>(g.members.size());
   std::vector<TuneKey> keys = {
-      std::make_tuple(ctx->device, static_cast<int>(OP_SYRK_IN), f32 ? 1 : 0, g.Mp, g.Mp, cnt),
+      std::make_tuple(ctx->device, static_cast<int>(OP_SYRK), f32 ? 1 : 0, g.Mp, g.Mp, cnt),
       std::make_tuple(ctx->device, static_cast<int>(OP_SYM), f32 ? 1 : 0, g.Mp, g.Mp, cnt),
       std::make_tuple(ctx->device, static_cast<int>(OP_APPLY), f32 ? 1 : 0, g.Mp, g.Np, cnt)};
-  if (more) keys.push_back(std::make_tuple(ctx->device, static_cast<int>(OP_SYRK), f32 ? 1 : 0, g.Mp, g.Mp, cnt));
   std::lock_guard<std::mutex> lk(g_tune_mu);
   for (const TuneKey& k : keys)
     if (g_tuned.find(k) == g_tuned.end()) return false;
@@ -631,41 +648,6 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
     return MUON_OK;
   }
 
-  // Momentum, canonical U (into X) and per-tile partial sums of squares.
-  MomentumParams mp;
-  std::memset(&mp, 0, sizeof(mp));
-  mp.table = table;
-  mp.U = X;
-  mp.sU = g.stride_x; mp.ldu = g.Np;
-  mp.m = static_cast<int32_t>(g.m); mp.n = static_cast<int32_t>(g.n);
-  mp.Mp = static_cast<int32_t>(g.Mp); mp.Np = static_cast<int32_t>(g.Np);
-  mp.tiles_m = g.mom_tiles_m; mp.tiles_n = g.mom_tiles_n;
-  mp.count = count;
-  mp.mu = hp.momentum; mp.nesterov = hp.nesterov;
-  mp.g_bf16 = hp.g_dtype == MUON_BF16; mp.m_bf16 = hp.m_dtype == MUON_BF16; mp.u_bf16 = !f32;
-  mp.partials = reinterpret_cast<float*>(env.ws + g.off_partials);
-  mp.has_tall = g.has_tall ? 1 : 0;
-  if (inline_descs(g)) {
-    mp.inl.n = count;
-    for (int i = 0; i < count; ++i) mp.inl.d[i] = host_desc[i];
-    mp.table_out = table;
-  }
-  {
-    // algorithmic bytes: G read, M read + write, U written
-    const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;
-    const double ub = f32 ? 4.0 : 2.0;
-    const double elems = static_cast<double>(count) * g.m * g.n;
-    StageTimer tm(env.ctx, env.st, ST_MOMENTUM, g.m, g.n, count, 0.0, elems * (gb + 2.0 * mb + ub));
-    MUON_HIP(launch_momentum(mp, env.st));
-    tm.done();
-  }
-  {
-    StageTimer tm(env.ctx, env.st, ST_FINALIZE, g.m, g.n, count, 0.0,
-                  4.0 * count * g.mom_tiles_m * g.mom_tiles_n);
-    MUON_HIP(launch_norm_finalize(mp.partials, g.mom_tiles_m * g.mom_tiles_n, count, hp.eps, s, env.st));
-    tm.done();
-  }
-
   // Scales of the bf16 path (powers of two, so exact): the iterate X and its transposed
   // copies are stored in fp16 multiplied by xs ~ sqrt(m' n') (entries ~ 1); the Gram-like
   // matrices (R, Q R, A) are stored multiplied by e ~ m' so their entries sit in fp16's
@@ -675,17 +657,46 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
   const float a = hp.a, b1 = hp.b / e, c1 = hp.c / (e * e);
   const float ixs = 1.0f / xs;
 
-  // X0^T = xs * s * U^T: the B operand of the first apply product.
+  // Momentum in two passes over G and M: partial sums of U^2, the norm, then M' and the
+  // normalised iterate X0 = xs * s * U in both layouts (X and XT[0]).
+  MomentumParams mp;
+  std::memset(&mp, 0, sizeof(mp));
+  mp.table = table;
+  mp.X = X; mp.XT = XT[0];
+  mp.sX = g.stride_x;
+  mp.m = static_cast<int32_t>(g.m); mp.n = static_cast<int32_t>(g.n);
+  mp.Mp = static_cast<int32_t>(g.Mp); mp.Np = static_cast<int32_t>(g.Np);
+  mp.tiles_m = g.mom_tiles_m; mp.tiles_n = g.mom_tiles_n;
+  mp.norm_blocks = g.norm_blocks;
+  mp.count = count;
+  mp.mu = hp.momentum; mp.nesterov = hp.nesterov;
+  mp.g_bf16 = hp.g_dtype == MUON_BF16; mp.m_bf16 = hp.m_dtype == MUON_BF16; mp.x_f16 = !f32;
+  mp.xscale = xs;
+  mp.s = s;
+  mp.partials = reinterpret_cast<float*>(env.ws + g.off_partials);
+  if (inline_descs(g)) {
+    mp.inl.n = count;
+    for (int i = 0; i < count; ++i) mp.inl.d[i] = host_desc[i];
+    mp.table_out = table;
+  }
+  const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;
+  const double xb = f32 ? 4.0 : 2.0;
+  const double elems = static_cast<double>(count) * g.m * g.n;
   {
-    TransposeParams tp;
-    std::memset(&tp, 0, sizeof(tp));
-    tp.U = X; tp.XT = XT[0];
-    tp.sU = g.stride_x; tp.sXT = g.stride_x;
-    tp.Mp = static_cast<int32_t>(g.Mp); tp.Np = static_cast<int32_t>(g.Np);
-    tp.count = count; tp.u_bf16 = !f32; tp.scale = xs; tp.s = s;
-    const double elems = static_cast<double>(count) * g.m * g.n;
-    StageTimer tm(env.ctx, env.st, ST_TRANSPOSE, g.m, g.n, count, 0.0, elems * (f32 ? 8.0 : 4.0));
-    MUON_HIP(launch_transpose_scale(tp, env.st));
+    // algorithmic bytes: G and M read
+    StageTimer tm(env.ctx, env.st, ST_MOMENTUM_NORM, g.m, g.n, count, 0.0, elems * (gb + mb));
+    MUON_HIP(launch_momentum_norm(mp, env.st));
+    tm.done();
+  }
+  {
+    StageTimer tm(env.ctx, env.st, ST_FINALIZE, g.m, g.n, count, 0.0, 4.0 * count * g.norm_blocks);
+    MUON_HIP(launch_norm_finalize(mp.partials, g.norm_blocks, count, hp.eps, s, env.st));
+    tm.done();
+  }
+  {
+    // algorithmic bytes: G and M read, M' written, X0 written in two layouts
+    StageTimer tm(env.ctx, env.st, ST_MOMENTUM, g.m, g.n, count, 0.0, elems * (gb + 2.0 * mb + 2.0 * xb));
+    MUON_HIP(launch_momentum_x(mp, env.st));
     tm.done();
   }
 
@@ -695,9 +706,9 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
     void* B = env.ws + g.off_sq[1];
     const int rounds = total_rounds(hp);
     for (int r = 0; r < rounds; ++r) {
-      const bool first = r == 0, last = r == rounds - 1;
-      // A' = e X X^T (first round: the momentum output, times s^2)
-      MUON_HIP(first ? syrk(g, env, X, A, e, 2, true) : syrk(g, env, X, A, e * ixs * ixs, 0, false));
+      const bool last = r == rounds - 1;
+      // A' = e X X^T
+      MUON_HIP(syrk(g, env, X, A, e * ixs * ixs));
       MUON_HIP(square(g, env, A, A, A, B, c1, b1, 0.0f));           // B = b A + c A^2
       // X' = a X + B X  (X taken from its transposed copy, which carries xs)
       MUON_HIP(apply(g, env, B, XT[cur], X, XT[cur ^ 1], ixs, a * ixs, xs, true, last, table));
@@ -709,8 +720,8 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
     void* T1 = env.ws + g.off_sq[2];
     void* T2 = env.ws + g.off_sq[3];
     for (int sgi = 0; sgi < hp.n_segments; ++sgi) {
-      const bool first = sgi == 0, last = sgi == hp.n_segments - 1;
-      MUON_HIP(first ? syrk(g, env, X, R, e, 2, true) : syrk(g, env, X, R, e * ixs * ixs, 0, false));
+      const bool last = sgi == hp.n_segments - 1;
+      MUON_HIP(syrk(g, env, X, R, e * ixs * ixs));
       MUON_HIP(square(g, env, R, R, R, Q, c1, b1, a));            // Q = P(R)
       for (int k = 1; k < hp.segments[sgi]; ++k) {
         MUON_HIP(square(g, env, Q, R, nullptr, T1, 1.0f, 0.0f, 0.0f));   // T = Q R
@@ -902,20 +913,23 @@ int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
 int muon_tune_save(muon_ctx* ctx, const char* path) {
   try {
     if (!ctx || !path) return MUON_ERR_ARG;
-    std::vector<std::pair<TuneKey, int>> rows;
+    std::vector<std::tuple<TuneKey, int, float>> rows;
     {
       std::lock_guard<std::mutex> lk(g_tune_mu);
       for (const auto& kv : g_tuned)
-        if (std::get<0>(kv.first) == ctx->device) rows.push_back(kv);
+        if (std::get<0>(kv.first) == ctx->device) {
+          auto t = g_tuned_ms.find(kv.first);
+          rows.emplace_back(kv.first, kv.second, t == g_tuned_ms.end() ? -1.0f : t->second);
+        }
     }
     FILE* f = std::fopen(path, "w");
     if (!f) return MUON_ERR_ARG;
     bool ok = true;
-    for (const auto& kv : rows) {
-      const TuneKey& k = kv.first;
-      ok = ok && std::fprintf(f, "%d %d %lld %lld %d %d\n", std::get<1>(k), std::get<2>(k),
+    for (const auto& row : rows) {
+      const TuneKey& k = std::get<0>(row);
+      ok = ok && std::fprintf(f, "%d %d %lld %lld %d %d %.9g\n", std::get<1>(k), std::get<2>(k),
                               static_cast<long long>(std::get<3>(k)), static_cast<long long>(std::get<4>(k)),
-                              std::get<5>(k), kv.second) > 0;
+                              std::get<5>(k), std::get<1>(row), static_cast<double>(std::get<2>(row))) > 0;
     }
     ok = (std::fclose(f) == 0) && ok;
     return ok ? MUON_OK : MUON_ERR_ARG;
@@ -930,20 +944,30 @@ int muon_tune_load(muon_ctx* ctx, const char* path, int* n_loaded) {
     if (!ctx || !path) return MUON_ERR_ARG;
     FILE* f = std::fopen(path, "r");
     if (!f) return MUON_ERR_ARG;
-    std::vector<std::pair<TuneKey, int>> rows;
+    std::vector<std::tuple<TuneKey, int, float>> rows;
     bool ok = true;
     char line[256];
     while (ok && std::fgets(line, sizeof(line), f)) {
       int op = 0, f32 = 0, cnt = 0, tile = 0, used = 0;
       long long mp = 0, np = 0;
+      float ms = -1.0f;
       bool blank = true;
       for (const char* c = line; *c; ++c)
         if (*c != ' ' && *c != '\t' && *c != '\n' && *c != '\r') blank = false;
       if (blank) continue;
-      if (std::sscanf(line, "%d %d %lld %lld %d %d %n", &op, &f32, &mp, &np, &cnt, &tile, &used) != 6 ||
-          line[used] != '\0') {
+      // six integers, then optionally the measured time in ms (negative: none)
+      const int got = std::sscanf(line, "%d %d %lld %lld %d %d %n", &op, &f32, &mp, &np, &cnt, &tile, &used);
+      if (got != 6) {
         ok = false;
         break;
+      }
+      if (line[used] != '\0') {
+        int used2 = 0;
+        if (std::sscanf(line + used, "%f %n", &ms, &used2) != 1 || line[used + used2] != '\0' ||
+            !std::isfinite(ms)) {
+          ok = false;
+          break;
+        }
       }
       const bool sym = op == OP_SYRK_IN || op == OP_SYM || op == OP_SYRK;
       ok = (sym || op == OP_APPLY) && (f32 == 0 || f32 == 1) && mp >= kPad && np >= kPad &&
@@ -951,13 +975,17 @@ int muon_tune_load(muon_ctx* ctx, const char* path, int* n_loaded) {
            cnt <= kMaxBatch && tile >= 0 && tile < TILE_COUNT && (!sym || mp == np) &&
            tile_available(sym, f32 == 1, tile);
       if (ok) rows.emplace_back(std::make_tuple(ctx->device, op, f32, static_cast<int64_t>(mp),
-                                                static_cast<int64_t>(np), cnt), tile);
+                                                static_cast<int64_t>(np), cnt), tile, ms);
     }
     ok = ok && !std::ferror(f);
     std::fclose(f);
     if (!ok) return MUON_ERR_ARG;
     std::lock_guard<std::mutex> lk(g_tune_mu);
-    for (const auto& kv : rows) g_tuned[kv.first] = kv.second;
+    for (const auto& row : rows) {
+      g_tuned[std::get<0>(row)] = std::get<1>(row);
+      if (std::get<2>(row) >= 0.0f) g_tuned_ms[std::get<0>(row)] = std::get<2>(row);
+      else g_tuned_ms.erase(std::get<0>(row));
+    }
     if (n_loaded) *n_loaded = static_cast<int>(rows.size());
     return MUON_OK;
   } catch (...) {

@@ -106,41 +106,40 @@ struct TableChunk {
   int32_t n;
 };
 
-// Momentum + canonical-orientation write of U + per-block partial sums of U^2.
+// The HBM-bound stages take two passes over G and M, so that the iterate is rounded once,
+// from the fp32 momentum output U, after the norm is known:
+//   launch_momentum_norm: per-block partial sums of U^2 (U = G + mu (mu M + G), or
+//     mu M + G without Nesterov) over the stored elements; nothing is written but the
+//     partials (and, with inline descriptors, the table);
+//   launch_momentum_x: M <- mu M + G, and the normalised iterate X0 = xscale * s[i] * U in
+//     the canonical orientation, written row-major (X, Mp x Np) and transposed (XT,
+//     Np x Mp), padding included (zeros); fp16 on the bf16 path, fp32 on the fp32 path.
 struct MomentumParams {
   const MatDesc* table;   // entry i = matrix i of the batch
-  void* U;                // canonical padded buffers, matrix i at U + i*sU (elements)
-  int64_t sU, ldu;        // element stride between matrices, leading dimension (= Np)
+  void* X;                // canonical padded iterate, matrix i at X + i*sX (elements)
+  void* XT;               // its transpose, matrix i at XT + i*sX (ld Mp)
+  int64_t sX;             // element stride between matrices (Mp * Np)
   int32_t m, n;           // canonical dims m' <= n'
   int32_t Mp, Np;         // padded canonical dims
-  int32_t tiles_m, tiles_n;  // 64 x 64 canonical tiles per matrix
+  int32_t tiles_m, tiles_n;  // 64 x 64 canonical tiles per matrix (momentum_x grid)
+  int32_t norm_blocks;    // 4096-element blocks of the stored matrix (momentum_norm grid)
   int32_t count;
   float mu;
   int32_t nesterov;
-  int32_t g_bf16, m_bf16, u_bf16;   // storage dtypes (0: fp32)
-  float* partials;        // [count][tiles_m*tiles_n]
-  int32_t has_tall;       // some matrix of the batch is stored transposed (rows > cols)
+  int32_t g_bf16, m_bf16;   // storage dtypes (0: fp32)
+  int32_t x_f16;            // iterate fp16 (bf16 path) or fp32
+  float xscale;             // power-of-two scale of the stored iterate
+  const float* s;           // per-matrix 1 / (||U||_F + eps) (momentum_x)
+  float* partials;          // [count][norm_blocks]
   // With inl.n > 0 (batches of at most kTableChunk matrices) the descriptors come in the
-  // kernel arguments and workgroup (0, i) also writes entry i to table_out, for the later
-  // stages of the batch; no separate table launch is needed.
+  // kernel arguments; momentum_norm's workgroup (0, i) also writes entry i to table_out,
+  // for the later stages of the batch, so no separate table launch is needed.
   TableChunk inl;
   MatDesc* table_out;
 };
-hipError_t launch_momentum(const MomentumParams& p, hipStream_t st);
-
-// XT[i] = scale * s[i] * U[i]^T: the transposed, scaled copy of the momentum output the
-// first apply product reads (fp16 on the bf16 path, fp32 on the fp32 path).
-struct TransposeParams {
-  const void* U;          // Mp x Np, ld Np, bf16 or fp32
-  void* XT;               // Np x Mp, ld Mp, fp16 or fp32
-  int64_t sU, sXT;        // element strides between matrices
-  int32_t Mp, Np;
-  int32_t count;
-  int32_t u_bf16;         // U bf16 (then XT fp16) or fp32 (then XT fp32)
-  float scale;
-  const float* s;
-};
-hipError_t launch_transpose_scale(const TransposeParams& p, hipStream_t st);
+hipError_t launch_momentum_norm(const MomentumParams& p, hipStream_t st);
+hipError_t launch_momentum_x(const MomentumParams& p, hipStream_t st);
+constexpr int kNormBlock = 4096;  // stored elements per partial sum
 
 // s[i] = 1 / (sqrt(sum_j partials[i][j]) + eps), fixed-order fp64 reduction.
 hipError_t launch_norm_finalize(const float* partials, int per_matrix, int count, float eps,

@@ -12,9 +12,10 @@
 //     transposed, and is streamed through an LDS staging buffer 64 columns (Gram product)
 //     or 64 rows of X^T (apply) at a time, the next slice's global loads in flight while
 //     the current one is multiplied.
-// Arithmetic and scaling follow the staged bf16 path: U as stored in bf16, the iterate kept
-// in fp16 as xs * X, Gram-space matrices in fp16 scaled by e (polynomial coefficients b / e
-// and c / e^2), fp32 MFMA accumulation (32x32x16 fp16). Products are dense.
+// Arithmetic and scaling follow the staged bf16 path: the iterate kept in fp16 as xs * X
+// (X0 rounded once from the fp32 momentum output), Gram-space matrices in fp16 scaled by e
+// (polynomial coefficients b / e and c / e^2), fp32 MFMA accumulation (32x32x16 fp16).
+// Products are dense.
 #include "internal.hpp"
 
 namespace muon {
@@ -138,69 +139,68 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
                 static_cast<u16*>(p.XT[1]) + static_cast<int64_t>(mat) * p.sXT};
 
   // 1. Momentum in the stored layout, 8 consecutive stored elements per thread (16-byte
-  //    accesses when rows allow); U (rounded to bf16, as the staged path stores it) goes to
-  //    LDS in the canonical layout (the recurrence's LDS is free until step 3); sum of
-  //    squares of the stored U. Every load of a group is issued before its stores.
-  u16* U = reinterpret_cast<u16*>(sm);   // MP x Np bf16, row-major
-  static_assert(sizeof(sm) >= static_cast<size_t>(kSmallMaxElems) * 2, "U fits in LDS");
+  //    accesses when rows allow), in two passes over G and M as on the staged path: the
+  //    first sums the squares of the fp32 U (fixed-order tree over the threads: the norm is
+  //    deterministic), the second stores M' and writes X0 = xs * s * U, rounded once to
+  //    fp16, to LDS in the canonical layout (the recurrence's LDS is free until step 3).
+  u16* U = reinterpret_cast<u16*>(sm);   // MP x Np fp16, row-major: xs * X0
+  static_assert(sizeof(sm) >= static_cast<size_t>(kSmallMaxElems) * 2, "X0 fits in LDS");
   {
     const int total = MP * Np;
     for (int i = tid * 8; i < total; i += NT * 8) *reinterpret_cast<uint4*>(U + i) = make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();
-  float sq = 0.0f;
-  {
-    const int rows = static_cast<int>(d.rows), cols = static_cast<int>(d.cols);
-    const int gpr = (cols + 7) / 8;            // groups of 8 per stored row
-    const bool vec = (cols % 8) == 0 && (reinterpret_cast<uintptr_t>(d.G) % 16) == 0 &&
-                     (reinterpret_cast<uintptr_t>(d.M) % 16) == 0;
-    for (int gi = tid; gi < rows * gpr; gi += NT) {
-      const int sr = gi / gpr, sc0 = (gi % gpr) * 8;
-      const int64_t base = static_cast<int64_t>(sr) * cols + sc0;
-      float g[8], m[8];
-      if (vec) {
-        if (p.g_bf16) {
-          const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const u16*>(d.G) + base);
-          const unsigned int ws[4] = {w.x, w.y, w.z, w.w};
+  const int rows = static_cast<int>(d.rows), cols = static_cast<int>(d.cols);
+  const int gpr = (cols + 7) / 8;            // groups of 8 per stored row
+  const bool vec = (cols % 8) == 0 && (reinterpret_cast<uintptr_t>(d.G) % 16) == 0 &&
+                   (reinterpret_cast<uintptr_t>(d.M) % 16) == 0;
+  // G and M of stored group gi (zero past the row end), the new momentum and U.
+  auto load_gm = [&](int gi, float (&g)[8], float (&m)[8]) {
+    const int sr = gi / gpr, sc0 = (gi % gpr) * 8;
+    const int64_t base = static_cast<int64_t>(sr) * cols + sc0;
+    if (vec) {
+      if (p.g_bf16) {
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const u16*>(d.G) + base);
+        const unsigned int ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) { g[2 * q] = __uint_as_float(ws[q] << 16); g[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u); }
-        } else {
-          const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(d.G) + base);
-          const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(d.G) + base + 4);
-          g[0] = x0.x; g[1] = x0.y; g[2] = x0.z; g[3] = x0.w; g[4] = x1.x; g[5] = x1.y; g[6] = x1.z; g[7] = x1.w;
-        }
-        if (p.m_bf16) {
-          const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const u16*>(d.M) + base);
-          const unsigned int ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { m[2 * q] = __uint_as_float(ws[q] << 16); m[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u); }
-        } else {
-          const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(d.M) + base);
-          const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(d.M) + base + 4);
-          m[0] = x0.x; m[1] = x0.y; m[2] = x0.z; m[3] = x0.w; m[4] = x1.x; m[5] = x1.y; m[6] = x1.z; m[7] = x1.w;
-        }
+        for (int q = 0; q < 4; ++q) { g[2 * q] = __uint_as_float(ws[q] << 16); g[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u); }
       } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const bool ok = sc0 + k < cols;
-          g[k] = ok ? load_elem(d.G, base + k, p.g_bf16) : 0.0f;
-          m[k] = ok ? load_elem(d.M, base + k, p.m_bf16) : 0.0f;
-        }
+        const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(d.G) + base);
+        const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(d.G) + base + 4);
+        g[0] = x0.x; g[1] = x0.y; g[2] = x0.z; g[3] = x0.w; g[4] = x1.x; g[5] = x1.y; g[6] = x1.z; g[7] = x1.w;
       }
-      float mn[8];
+      if (p.m_bf16) {
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const u16*>(d.M) + base);
+        const unsigned int ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) mn[k] = p.mu * m[k] + g[k];
+        for (int q = 0; q < 4; ++q) { m[2 * q] = __uint_as_float(ws[q] << 16); m[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u); }
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(d.M) + base);
+        const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(d.M) + base + 4);
+        m[0] = x0.x; m[1] = x0.y; m[2] = x0.z; m[3] = x0.w; m[4] = x1.x; m[5] = x1.y; m[6] = x1.z; m[7] = x1.w;
+      }
+    } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        if (sc0 + k >= cols) continue;
-        store_elem(d.M, base + k, mn[k], p.m_bf16);
-        const u16 ub = f32_to_bf16(p.nesterov ? g[k] + p.mu * mn[k] : mn[k]);
-        const float u = bf16_to_f32(ub);
-        sq += u * u;
-        const int r = d.transposed ? sc0 + k : sr, c = d.transposed ? sr : sc0 + k;
-        U[r * Np + c] = ub;
+        const bool ok = sc0 + k < cols;
+        g[k] = ok ? load_elem(d.G, base + k, p.g_bf16) : 0.0f;
+        m[k] = ok ? load_elem(d.M, base + k, p.m_bf16) : 0.0f;
       }
     }
+  };
+  auto momentum8 = [&](const float (&g)[8], const float (&m)[8], float (&mn)[8], float (&u)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      mn[k] = p.mu * m[k] + g[k];
+      u[k] = p.nesterov ? g[k] + p.mu * mn[k] : mn[k];
+    }
+  };
+  float sq = 0.0f;
+  for (int gi = tid; gi < rows * gpr; gi += NT) {
+    float g[8], m[8], mn[8], u[8];
+    load_gm(gi, g, m);
+    momentum8(g, m, mn, u);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sq += u[k] * u[k];   // zero past the row end
   }
   red[tid] = static_cast<double>(sq);
   __syncthreads();
@@ -209,27 +209,36 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
     __syncthreads();
   }
   const float s = static_cast<float>(1.0 / (sqrt(red[0]) + static_cast<double>(p.eps)));
+  const float xsc = p.xs * s;
+  for (int gi = tid; gi < rows * gpr; gi += NT) {
+    float g[8], m[8], mn[8], u[8];
+    load_gm(gi, g, m);
+    momentum8(g, m, mn, u);
+    const int sr = gi / gpr, sc0 = (gi % gpr) * 8;
+    const int64_t base = static_cast<int64_t>(sr) * cols + sc0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (sc0 + k >= cols) continue;
+      store_elem(d.M, base + k, mn[k], p.m_bf16);
+      const int r = d.transposed ? sc0 + k : sr, c = d.transposed ? sr : sc0 + k;
+      U[r * Np + c] = f32_to_f16(xsc * u[k]);
+    }
+  }
+  __syncthreads();
 
-  // 2. The iterate xs * s * U in fp16 to the workspace, row-major and transposed, 8
-  //    elements (16 bytes) per store.
+  // 2. The iterate (already xs * X0 in fp16) to the workspace, row-major and transposed,
+  //    8 elements (16 bytes) per store.
   {
-    const float xsc = p.xs * s;
     for (int i = tid * 8; i < MP * Np; i += NT * 8) {
       const int r = i / Np, c0 = i % Np;
-      unsigned int w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        w[q] = f32_to_f16(bf16_to_f32(U[i + 2 * q]) * xsc) |
-               (static_cast<unsigned int>(f32_to_f16(bf16_to_f32(U[i + 2 * q + 1]) * xsc)) << 16);
-      *reinterpret_cast<uint4*>(X + static_cast<int64_t>(r) * Np + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(X + static_cast<int64_t>(r) * Np + c0) = *reinterpret_cast<const uint4*>(U + i);
     }
     for (int i = tid * 8; i < MP * Np; i += NT * 8) {   // X^T: row c holds column c of X
       const int c = i / MP, r0 = i % MP;
       unsigned int w[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        w[q] = f32_to_f16(bf16_to_f32(U[(r0 + 2 * q) * Np + c]) * xsc) |
-               (static_cast<unsigned int>(f32_to_f16(bf16_to_f32(U[(r0 + 2 * q + 1) * Np + c]) * xsc)) << 16);
+        w[q] = U[(r0 + 2 * q) * Np + c] | (static_cast<unsigned int>(U[(r0 + 2 * q + 1) * Np + c]) << 16);
       *reinterpret_cast<uint4*>(XT[0] + static_cast<int64_t>(c) * MP + r0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }

@@ -176,10 +176,26 @@ def custom(name: str, shapes, *, structure="gaussian", dtype="bf16", rank=8, dec
                     rank=rank, decay=decay, steps=steps)
 
 
+def _haar_torch(Z):
+    """Orthonormal factor of the QR decomposition of the Gaussian n x r matrix Z with R's
+    diagonal positive (the same basis :func:`haar_basis` takes, as that factorisation is
+    unique), by Cholesky QR: the r x r Gram matrix is formed on the device in float64, its
+    Cholesky factor R^T computed on the host (NumPy), and Q = Z R^-1 on the device. Only
+    products and element-wise kernels run on the device (Z is well conditioned for
+    n >> r, so Cholesky QR keeps Q orthonormal to float64 rounding)."""
+    import torch
+
+    Z64 = Z.to(torch.float64)
+    gram = (Z64.T @ Z64).cpu().numpy()
+    Rinv = np.linalg.inv(np.linalg.cholesky(gram).T)      # upper-triangular R^-1
+    return (Z64 @ torch.from_numpy(Rinv).to(Z.device)).to(torch.float32)
+
+
 def gradient_torch(w: Workload, step: int, index: int, device="cuda", spec: MatrixSpec | None = None):
     """Device-side draw with the same recipe as :func:`gradient_np` (torch's generator,
     so not the same values): for timing runs of workloads too large to draw on the host.
-    Returns a tensor in the gradient's storage dtype."""
+    The Haar bases come from :func:`_haar_torch` (no device linear-algebra solver is
+    called). Returns a tensor in the gradient's storage dtype."""
     import torch
 
     spec = spec or w.matrices[index]
@@ -190,10 +206,8 @@ def gradient_torch(w: Workload, step: int, index: int, device="cuda", spec: Matr
         G = torch.randn(rows, cols, generator=gen, device=device)
     else:
         r = min(w.rank, rows, cols)
-        Ub, Rb = torch.linalg.qr(torch.randn(rows, r, generator=gen, device=device))
-        Ub = Ub * torch.sign(torch.diagonal(Rb))
-        Vb, Rv = torch.linalg.qr(torch.randn(cols, r, generator=gen, device=device))
-        Vb = Vb * torch.sign(torch.diagonal(Rv))
+        Ub = _haar_torch(torch.randn(rows, r, generator=gen, device=device))
+        Vb = _haar_torch(torch.randn(cols, r, generator=gen, device=device))
         s = w.scale * torch.arange(1, r + 1, device=device, dtype=torch.float32) ** (-w.decay)
         G = (Ub * s) @ Vb.T
         G += w.noise * torch.randn(rows, cols, generator=gen, device=device)

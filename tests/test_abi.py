@@ -259,20 +259,24 @@ def test_tune_cache_round_trip(hctx, tmp_path):
     """Choices loaded from a file are the ones plan_info reports and are written back
     unchanged (a host-only context keeps its own device key, so GPU runs are unaffected)."""
     src = tmp_path / "tune.txt"
-    src.write_text("1 0 2560 2560 1 10\n2 0 2560 9728 1 7\n\n0 0 2560 2560 1 5\n4 0 2560 2560 1 12\n")
+    src.write_text("1 0 2560 2560 1 10 0.0305\n2 0 2560 9728 1 7\n\n0 0 2560 2560 1 5 -1\n"
+                   "4 0 2560 2560 1 12 0.0925\n")
     assert B.muon_tune_load(hctx, str(src)) == 4
     e = B.muon_plan_info(hctx, [(0, 0, 0, 2560, 9728)], B.make_hparams(), 0)
     assert (e.tile_sym, e.tile_apply) == (10, 7)
     out = tmp_path / "out.txt"
     B.muon_tune_save(hctx, str(out))
-    got = sorted(tuple(map(int, l.split())) for l in out.read_text().splitlines())
-    assert got == sorted([(0, 0, 2560, 2560, 1, 5), (1, 0, 2560, 2560, 1, 10), (2, 0, 2560, 9728, 1, 7),
-                          (4, 0, 2560, 2560, 1, 12)])
+    # the time is held as a float32
+    got = sorted((tuple(map(int, l.split()[:6])), round(float(l.split()[6]), 6)) for l in out.read_text().splitlines())
+    assert got == sorted([((0, 0, 2560, 2560, 1, 5), -1.0), ((1, 0, 2560, 2560, 1, 10), 0.0305),
+                          ((2, 0, 2560, 9728, 1, 7), -1.0), ((4, 0, 2560, 2560, 1, 12), 0.0925)])
 
 
 @pytest.mark.parametrize("text", [
     "1 0 2560 2560 1\n",            # missing field
-    "1 0 2560 2560 1 10 3\n",       # extra field
+    "1 0 2560 2560 1 10 3 4\n",     # extra field after the time
+    "1 0 2560 2560 1 10 nan\n",     # time not finite
+    "1 0 2560 2560 1 10 t\n",       # time not a number
     "3 0 2560 9728 1 7\n",          # the update stage shares the apply's choice
     "1 0 2560 9728 1 10\n",         # symmetric stage with m != n
     "1 0 2560 2560 1 6\n",          # 256x128 tile for a symmetric stage

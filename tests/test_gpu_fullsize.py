@@ -6,8 +6,9 @@ Inputs are the workloads' device-side draws (workloads.gradient_torch / weight_t
 the sampled matrices' inputs are copied to the host before the step and read exactly
 (bf16 / fp32 values are exact in float64), so the oracle never sees a value the library
 computed. Bars as in test_gpu_parity: O by relative Frobenius error <= 2e-2, M' to its
-storage rounding. Set MUON_FULL_PARITY=1 to also check a seeded 10% sample of every
-other matrix (slow: minutes of fp64 work on the host).
+storage rounding. Besides whole layers, a seeded 10% sample of the other matrices is
+checked; MUON_FULL_PARITY=1 checks every matrix (slow: tens of minutes of fp64 work on
+the host).
 """
 
 import os
@@ -81,12 +82,19 @@ class FullRun:
         self.B.muon_destroy(self.ctx)
 
 
-def sample(w, layers, per_layer):
-    idx = [l * per_layer + j for l in layers for j in range(per_layer)]
+def sample(w, layers, per_layer, checked_layers, extra=False):
+    """Every matrix of `layers`, plus (extra=True) a seeded 10% sample of the matrices
+    outside `checked_layers` (all the layers the workload's tests check in full), so the
+    layer tests and the sample together cover distinct matrices. MUON_FULL_PARITY=1 checks
+    every matrix instead."""
     if os.environ.get("MUON_FULL_PARITY") == "1":
+        return list(range(len(w.matrices))) if extra else []
+    idx = [l * per_layer + j for l in layers for j in range(per_layer)]
+    if extra:
+        done = {l * per_layer + j for l in checked_layers for j in range(per_layer)}
+        rest = [i for i in range(len(w.matrices)) if i not in done]
         rng = np.random.default_rng(w.wid)
-        rest = [i for i in range(len(w.matrices)) if i not in idx]
-        idx += sorted(rng.choice(rest, size=max(1, len(rest) // 10), replace=False).tolist())
+        idx += sorted(rng.choice(rest, size=(len(w.matrices) + 9) // 10, replace=False).tolist())
     return idx
 
 
@@ -137,13 +145,14 @@ def dense7b(B):
 
 def test_decoder_24_layers_three_steps(decoder):
     """168 matrices (2048^2 plain, 8192x2048 / 2048x8192 Gram), 3 steps with momentum
-    carried; layers 0 and 23 checked after every step."""
-    run_and_check(decoder, sample(decoder.w, [0, 23], 7), steps=3)
+    carried; layers 0 and 23 and a seeded 10% of the rest checked after every step."""
+    run_and_check(decoder, sample(decoder.w, [0, 23], 7, [0, 23], extra=True), steps=3)
 
 
 @pytest.mark.parametrize("layer", [0, 27])
 def test_dense_7b_one_step(dense7b, layer):
     """196 matrices (3584^2 plain; 512x3584 and 3584x18944 / 18944x3584 Gram); every matrix
-    of one layer checked."""
+    of one layer checked; the layer-0 run also checks a seeded 10% of the other layers'
+    matrices (20 of them: 34 distinct matrices over the two runs)."""
     dense7b.reset()
-    run_and_check(dense7b, sample(dense7b.w, [layer], 7), steps=1)
+    run_and_check(dense7b, sample(dense7b.w, [layer], 7, [0, 27], extra=layer == 0), steps=1)

@@ -247,16 +247,19 @@ def ctx_staged(B):
     B.muon_destroy(c)
 
 
+@pytest.mark.parametrize("structure", ["gaussian", "lowrank"])
 @pytest.mark.parametrize("mode", ["gram", "plain"])
-def test_small_shapes_both_paths(B, ctx, ctx_staged, mode):
+def test_small_shapes_both_paths(B, ctx, ctx_staged, mode, structure):
     """Shapes the single-workgroup kernel takes (padded m' <= 128 and m' n' <= 64 Ki; 1 x 17
-    up to 128 x 512 and 64 x 1024, tall and wide, ragged), on it and on the staged kernels: both within the bar of the oracle, over
-    two steps with momentum carried."""
+    up to 128 x 512 and 64 x 1024, tall and wide, ragged), on it and on the staged kernels:
+    both within the bar of the oracle, over two steps with momentum carried. Gradients are
+    i.i.d. (the small-matrix workload) or rank 4 (s_i = 10 / i) plus N(0, 0.01^2) noise:
+    there Newton-Schulz lifts the noise directions, whose singular values are ~100x below
+    the top one, to the size of the signal, so an error of a 16-bit rounding of U in them
+    shows in O (rounding U to bf16 before the norm gave 0.9-1.7e-2 on these shapes)."""
     shapes = [(1, 17), (64, 256), (256, 64), (100, 300), (65, 500), (128, 128), (7, 129), (128, 512),
               (64, 1024), (1000, 60)]
-    # i.i.d. gradients as in the small-matrix workload (a rank-4 gradient plus 1% noise on
-    # these shapes puts the bf16 rounding of U above the bar on both paths alike)
-    w = wl.custom("small_both", shapes, structure="gaussian", wid=213, steps=2)
+    w = wl.custom("small_both", shapes, structure=structure, rank=4, wid=213, steps=2)
     hp = B.make_hparams(mode=mode)
     raw = [(0, 0, 0, r, c) for r, c in shapes]
     assert all(B.muon_plan_info(ctx, raw, hp, i).single_wg == 1 for i in range(len(shapes)))
@@ -316,7 +319,11 @@ def test_zero_gradient_and_determinism(B, ctx):
         Wn = to_np(st.W[k])
         assert np.all(np.isfinite(Wn))
         assert np.allclose(Wn, W0[k] * (1 - 0.02 * 0.1), rtol=1e-6, atol=0)
-    # identical inputs -> bitwise identical outputs (fixed-order reductions)
+    # identical inputs -> bitwise identical outputs (fixed-order reductions); a first step
+    # measures the tiles and stage times, from which the dispatcher's choice is fixed
+    warm = GpuState(wl.custom("det", [(192, 640), (640, 192)], structure="lowrank", rank=4, wid=208))
+    warm.load_gradients(0)
+    run_step(ctx, warm, B.make_hparams())
     outs = []
     for _ in range(2):
         st2 = GpuState(wl.custom("det", [(192, 640), (640, 192)], structure="lowrank", rank=4, wid=208))

@@ -195,6 +195,24 @@ int muon_workspace_size(muon_ctx *ctx, const muon_matrix *mats, int count,
 int muon_step(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hparams *hp,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same update as muon_step, with the
+ * scratch space in a library-owned device array of MUON_STATIC_SCRATCH_BYTES instead of a
+ * workspace argument. Each GPU the library initialises a context on holds its own copy of
+ * the array (reserved when the library's code is loaded on the device, looked up by
+ * muon_init) until the process ends. A list whose muon_workspace_size exceeds the array
+ * returns MUON_ERR_WORKSPACE before anything is launched. The call allocates nothing and
+ * creates no HIP object: it measures no tiles (it uses the choices muon_step measured or
+ * loaded for the same shapes, else the static ones), records no profiler events and runs
+ * every group on `stream`; the scratch holds nothing that must start at zero. Every call on
+ * one GPU shares that GPU's array: calls whose work overlaps on one GPU (on different
+ * streams, or from different contexts or threads without ordering) race and corrupt each
+ * other's results; calls ordered on one stream do not. Results equal muon_step's bitwise
+ * when the tile choices are the same. */
+#define MUON_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+int muon_step_static(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hparams *hp,
+                     void *stream);
+
 /* Measured tile choices, shared by every context of the process, to and from a text file,
  * so that another process starts with the same choices instead of measuring again
  * (DMuon summary, section 2.4: per-shape configurations measured once and cached). One

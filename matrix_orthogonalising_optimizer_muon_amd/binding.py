@@ -103,6 +103,10 @@ _lib.muon_workspace_size.restype = ctypes.c_int
 _lib.muon_step.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int,
                            ctypes.POINTER(muon_hparams), _P, ctypes.c_size_t, _P]
 _lib.muon_step.restype = ctypes.c_int
+_lib.muon_step_static.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int,
+                                  ctypes.POINTER(muon_hparams), _P]
+_lib.muon_step_static.restype = ctypes.c_int
+MUON_STATIC_SCRATCH_BYTES = 256 << 20
 _lib.muon_plan_info.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int,
                                 ctypes.POINTER(muon_hparams), ctypes.c_int,
                                 ctypes.POINTER(muon_plan_entry)]
@@ -248,6 +252,17 @@ def muon_step(ctx, mats, hp: muon_hparams, workspace_ptr: int, workspace_bytes: 
                           ctypes.c_size_t(workspace_bytes), ctypes.c_void_p(stream_ptr))
 
 
+def muon_step_static(ctx, mats, hp: muon_hparams, stream_ptr: int | None = None,
+                     count: int | None = None) -> int:
+    """Enqueue one update over the library's static scratch (no workspace); returns the
+    status (use ``check`` to raise)."""
+    arr = mats if isinstance(mats, ctypes.Array) else matrix_list(mats, hp)
+    n = len(mats) if count is None else count
+    if stream_ptr is None:
+        stream_ptr = torch.cuda.current_stream().cuda_stream
+    return _lib.muon_step_static(ctx, arr, n, ctypes.byref(hp), ctypes.c_void_p(stream_ptr))
+
+
 def muon_plan_info(ctx, mats, hp: muon_hparams, index: int) -> muon_plan_entry:
     arr = mats if isinstance(mats, ctypes.Array) else matrix_list(mats)
     out = muon_plan_entry()
@@ -337,7 +352,7 @@ def muon_destroy(ctx) -> int:
 
 def exported_symbols() -> list:
     """Names of the C entry points this binding resolved (each must exist in the .so)."""
-    return [n for n in ("muon_hparams_default", "muon_init", "muon_workspace_size", "muon_step",
+    return [n for n in ("muon_hparams_default", "muon_init", "muon_workspace_size", "muon_step", "muon_step_static",
                         "muon_plan_info", "muon_debug_gemm", "muon_profile_read", "muon_tune_save",
                         "muon_tune_load", "muon_adamw_hparams_default", "muon_adamw_step",
                         "muon_destroy", "muon_status_str")

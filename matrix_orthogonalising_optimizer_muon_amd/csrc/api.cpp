@@ -299,6 +299,9 @@ struct StepEnv {
   bool f32;
   const muon_hparams* hp;
   muon_ctx* ctx;
+  // muon_step_static: no tile measurement (cached choices or the static ones), no
+  // profiler events, one stream; nothing is created or allocated.
+  bool no_alloc = false;
 };
 
 // One stage name per kernel: "momentum_norm" the first pass over G and M (partial sums of
@@ -308,6 +311,8 @@ constexpr const char* kStageNames[] = {"table", "momentum", "norm_finalize", "mo
 enum Stage { ST_TABLE, ST_MOMENTUM, ST_FINALIZE, ST_MOMENTUM_NORM, ST_SYRK, ST_SQUARE, ST_APPLY, ST_UPDATE,
              ST_SINGLE_WG };
 constexpr size_t kMaxRecords = 1 << 16;
+
+inline muon_ctx* timer_ctx(const StepEnv& env) { return env.no_alloc ? nullptr : env.ctx; }
 
 // Brackets one launch with events when profiling is on (no effect otherwise).
 struct StageTimer {
@@ -430,7 +435,7 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
       auto it = g_tuned.find(key);
       if (it != g_tuned.end()) { cfg = it->second; found = true; }
     }
-    if (!found) {
+    if (!found && !env.no_alloc) {
       // Each candidate: one warm-up and four timed launches, its time the fastest of them.
       // The timed launches run in four passes over the candidates, alternately in forward
       // and in reverse order: back-to-back MFMA work lowers the clock under the power limit
@@ -500,7 +505,7 @@ hipError_t syrk(const Group& g, const StepEnv& env, const void* X, void* R, floa
     return p;
   };
   const double cnt = static_cast<double>(g.members.size());
-  StageTimer tm(env.ctx, env.st, ST_SYRK, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.n, 0.0);
+  StageTimer tm(timer_ctx(env), env.st, ST_SYRK, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.n, 0.0);
   const hipError_t e = run_stage(env, g, OP_SYRK, g.tile_sq, true, build, &tm.rec.tile);
   tm.done();
   return e;
@@ -521,7 +526,7 @@ hipError_t square(const Group& g, const StepEnv& env, const void* A, const void*
     return p;
   };
   const double cnt = static_cast<double>(g.members.size());
-  StageTimer tm(env.ctx, env.st, ST_SQUARE, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.m, 0.0);
+  StageTimer tm(timer_ctx(env), env.st, ST_SQUARE, g.m, g.n, static_cast<int>(cnt), cnt * g.m * g.m * g.m, 0.0);
   const hipError_t e = run_stage(env, g, OP_SYM, g.tile_sq, true, build, &tm.rec.tile);
   tm.done();
   return e;
@@ -553,7 +558,7 @@ hipError_t apply(const Group& g, const StepEnv& env, const void* Q, const void* 
   };
   const double cnt = static_cast<double>(g.members.size());
   const double wbytes = update ? cnt * g.m * g.n * 2.0 * (env.hp->w_dtype == MUON_BF16 ? 2.0 : 4.0) : 0.0;
-  StageTimer tm(env.ctx, env.st, update ? ST_UPDATE : ST_APPLY, g.m, g.n, static_cast<int>(cnt),
+  StageTimer tm(timer_ctx(env), env.st, update ? ST_UPDATE : ST_APPLY, g.m, g.n, static_cast<int>(cnt),
                 cnt * 2.0 * g.m * g.m * g.n, wbytes);
   const hipError_t e = run_stage(env, g, update ? OP_UPDATE : OP_APPLY, g.tile_ap, false, build, &tm.rec.tile);
   tm.done();
@@ -641,7 +646,7 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
     sp.g_bf16 = hp.g_dtype == MUON_BF16; sp.m_bf16 = hp.m_dtype == MUON_BF16; sp.w_bf16 = hp.w_dtype == MUON_BF16;
     const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;
     const double wb = hp.w_dtype == MUON_BF16 ? 2.0 : 4.0;
-    StageTimer tm(env.ctx, env.st, ST_SINGLE_WG, g.m, g.n, count, dense_flops(g.m, g.n, g.mode, hp) * count,
+    StageTimer tm(timer_ctx(env), env.st, ST_SINGLE_WG, g.m, g.n, count, dense_flops(g.m, g.n, g.mode, hp) * count,
                   static_cast<double>(count) * g.m * g.n * (gb + 2.0 * mb + 2.0 * wb));
     MUON_HIP(launch_small_ns(sp, env.st));
     tm.done();
@@ -684,18 +689,18 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
   const double elems = static_cast<double>(count) * g.m * g.n;
   {
     // algorithmic bytes: G and M read
-    StageTimer tm(env.ctx, env.st, ST_MOMENTUM_NORM, g.m, g.n, count, 0.0, elems * (gb + mb));
+    StageTimer tm(timer_ctx(env), env.st, ST_MOMENTUM_NORM, g.m, g.n, count, 0.0, elems * (gb + mb));
     MUON_HIP(launch_momentum_norm(mp, env.st));
     tm.done();
   }
   {
-    StageTimer tm(env.ctx, env.st, ST_FINALIZE, g.m, g.n, count, 0.0, 4.0 * count * g.norm_blocks);
+    StageTimer tm(timer_ctx(env), env.st, ST_FINALIZE, g.m, g.n, count, 0.0, 4.0 * count * g.norm_blocks);
     MUON_HIP(launch_norm_finalize(mp.partials, g.norm_blocks, count, hp.eps, s, env.st));
     tm.done();
   }
   {
     // algorithmic bytes: G and M read, M' written, X0 written in two layouts
-    StageTimer tm(env.ctx, env.st, ST_MOMENTUM, g.m, g.n, count, 0.0, elems * (gb + 2.0 * mb + 2.0 * xb));
+    StageTimer tm(timer_ctx(env), env.st, ST_MOMENTUM, g.m, g.n, count, 0.0, elems * (gb + 2.0 * mb + 2.0 * xb));
     MUON_HIP(launch_momentum_x(mp, env.st));
     tm.done();
   }
@@ -748,6 +753,119 @@ struct DeviceGuard {
   }
 };
 
+
+// File-scope scratch for muon_step_static (callers that cannot allocate device memory).
+// Each device holds its own copy; host code uses only the per-device address that
+// hipGetSymbolAddress returned for it (the array's name is not a device address on the
+// host).
+constexpr size_t kStaticScratchBytes = MUON_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_err[kMaxDevices] = {};
+
+// Called by muon_init once per device, with that device current.
+void init_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[device]) return;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e == hipSuccess && ptr) g_scratch_ptr[device] = ptr;
+  else g_scratch_err[device] = e == hipSuccess ? hipErrorInvalidSymbol : e;
+}
+
+void* scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
+
+int step_impl(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams* hp, void* workspace,
+              size_t workspace_bytes, void* stream, bool no_alloc) {
+  {
+    if (!ctx || count < 0 || (count > 0 && !mats)) return MUON_ERR_ARG;
+    const int rc = validate_hparams(hp);
+    if (rc != MUON_OK) return rc;
+    if (count == 0) return MUON_OK;
+    Plan plan;
+    const int pc = build_plan(ctx, mats, count, *hp, true, plan);
+    if (pc != MUON_OK) return pc;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 ||
+        workspace_bytes < plan.bytes)
+      return MUON_ERR_WORKSPACE;
+    if (ctx->device < 0) return MUON_ERR_DEVICE;
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return MUON_ERR_HIP;
+    StepEnv env{static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
+                hp->ns_dtype == MUON_F32, hp, ctx, no_alloc};
+    MatDesc* table = reinterpret_cast<MatDesc*>(env.ws + plan.off_table);
+    // Descriptor table, ordered by group, written by small kernels (no host sync).
+    std::vector<MatDesc> descs(count);
+    for (const Group& g : plan.groups) {
+      for (size_t i = 0; i < g.members.size(); ++i) {
+        const muon_matrix& mt = mats[g.members[i]];
+        MatDesc d{};
+        d.W = mt.W; d.G = mt.G; d.M = mt.M;
+        d.rows = mt.rows; d.cols = mt.cols;
+        d.transposed = mt.rows > mt.cols ? 1 : 0;
+        descs[g.table_base + i] = d;
+      }
+    }
+    // Groups with inline descriptors get their entries from their momentum kernel.
+    for (const Group& g : plan.groups) {
+      if (inline_descs(g)) continue;
+      const int base = g.table_base, n = static_cast<int>(g.members.size());
+      for (int b = 0; b < n; b += kTableChunk) {
+        TableChunk c;
+        std::memset(&c, 0, sizeof(c));
+        c.n = std::min(kTableChunk, n - b);
+        for (int i = 0; i < c.n; ++i) c.d[i] = descs[base + b + i];
+        StageTimer tm(timer_ctx(env), env.st, ST_TABLE, 0, 0, c.n, 0.0, sizeof(MatDesc) * c.n);
+        MUON_HIP(launch_write_table(c, table + base + b, env.st));
+        tm.done();
+      }
+    }
+    // Independent shape groups run on up to kMaxLanes streams (largest work first, each
+    // to the least loaded lane) when none of them still has tiles to measure and the
+    // context does not profile; otherwise all run on the caller's stream in order.
+    int nl = std::min<int>(kMaxLanes, static_cast<int>(plan.groups.size()));
+    if ((ctx->flags & MUON_FLAG_PROFILE) || no_alloc) nl = 1;
+    for (size_t i = 0; nl > 1 && i < plan.groups.size(); ++i)
+      if (!group_tuned(ctx, plan.groups[i], *hp, env.f32)) nl = 1;
+    if (nl > 1 && !ensure_lanes(ctx, nl)) nl = 1;
+    if (nl == 1) {
+      for (const Group& g : plan.groups) {
+        const int r = run_group(g, env, table + g.table_base, descs.data() + g.table_base);
+        if (r != MUON_OK) return r;
+      }
+      return MUON_OK;
+    }
+    MUON_HIP(hipEventRecord(ctx->lane_fork, env.st));
+    for (int l = 0; l < nl - 1; ++l) MUON_HIP(hipStreamWaitEvent(ctx->lanes[l], ctx->lane_fork, 0));
+    std::vector<double> load(nl, 0.0);
+    int r = MUON_OK;
+    for (const Group& g : plan.groups) {
+      const int l = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+      load[l] += g.work;
+      StepEnv le = env;
+      if (l > 0) le.st = ctx->lanes[l - 1];
+      r = run_group(g, le, table + g.table_base, descs.data() + g.table_base);
+      if (r != MUON_OK) break;
+    }
+    // The caller's stream waits for every lane, also after a failed launch, so nothing
+    // the step enqueued outlives the caller's view of the stream.
+    for (int l = 0; l < nl - 1; ++l) {
+      if (hipEventRecord(ctx->lane_join[l], ctx->lanes[l]) != hipSuccess ||
+          hipStreamWaitEvent(env.st, ctx->lane_join[l], 0) != hipSuccess)
+        r = MUON_ERR_HIP;
+    }
+    return r;
+  }
+}
+
+
 }  // namespace
 }  // namespace muon
 
@@ -797,6 +915,11 @@ int muon_init(muon_ctx** out, int device, uint32_t flags) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) return MUON_ERR_DEVICE;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MUON_ERR_DEVICE;
+    {
+      DeviceGuard dg(device);
+      if (!dg.ok) return MUON_ERR_HIP;
+      init_scratch(device);
+    }
     muon_ctx* c = new (std::nothrow) muon_ctx;
     if (!c) return MUON_ERR_HIP;
     c->device = device;
@@ -828,6 +951,15 @@ int muon_workspace_size(muon_ctx* ctx, const muon_matrix* mats, int count, const
 int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams* hp,
               void* workspace, size_t workspace_bytes, void* stream) {
   try {
+    return step_impl(ctx, mats, count, hp, workspace, workspace_bytes, stream, false);
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+int muon_step_static(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams* hp,
+                     void* stream) {
+  try {
     if (!ctx || count < 0 || (count > 0 && !mats)) return MUON_ERR_ARG;
     const int rc = validate_hparams(hp);
     if (rc != MUON_OK) return rc;
@@ -835,76 +967,11 @@ int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
     Plan plan;
     const int pc = build_plan(ctx, mats, count, *hp, true, plan);
     if (pc != MUON_OK) return pc;
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 ||
-        workspace_bytes < plan.bytes)
-      return MUON_ERR_WORKSPACE;
+    if (plan.bytes > kStaticScratchBytes) return MUON_ERR_WORKSPACE;
     if (ctx->device < 0) return MUON_ERR_DEVICE;
-    DeviceGuard dg(ctx->device);
-    if (!dg.ok) return MUON_ERR_HIP;
-    StepEnv env{static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
-                hp->ns_dtype == MUON_F32, hp, ctx};
-    MatDesc* table = reinterpret_cast<MatDesc*>(env.ws + plan.off_table);
-    // Descriptor table, ordered by group, written by small kernels (no host sync).
-    std::vector<MatDesc> descs(count);
-    for (const Group& g : plan.groups) {
-      for (size_t i = 0; i < g.members.size(); ++i) {
-        const muon_matrix& mt = mats[g.members[i]];
-        MatDesc d{};
-        d.W = mt.W; d.G = mt.G; d.M = mt.M;
-        d.rows = mt.rows; d.cols = mt.cols;
-        d.transposed = mt.rows > mt.cols ? 1 : 0;
-        descs[g.table_base + i] = d;
-      }
-    }
-    // Groups with inline descriptors get their entries from their momentum kernel.
-    for (const Group& g : plan.groups) {
-      if (inline_descs(g)) continue;
-      const int base = g.table_base, n = static_cast<int>(g.members.size());
-      for (int b = 0; b < n; b += kTableChunk) {
-        TableChunk c;
-        std::memset(&c, 0, sizeof(c));
-        c.n = std::min(kTableChunk, n - b);
-        for (int i = 0; i < c.n; ++i) c.d[i] = descs[base + b + i];
-        StageTimer tm(ctx, env.st, ST_TABLE, 0, 0, c.n, 0.0, sizeof(MatDesc) * c.n);
-        MUON_HIP(launch_write_table(c, table + base + b, env.st));
-        tm.done();
-      }
-    }
-    // Independent shape groups run on up to kMaxLanes streams (largest work first, each
-    // to the least loaded lane) when none of them still has tiles to measure and the
-    // context does not profile; otherwise all run on the caller's stream in order.
-    int nl = std::min<int>(kMaxLanes, static_cast<int>(plan.groups.size()));
-    if (ctx->flags & MUON_FLAG_PROFILE) nl = 1;
-    for (size_t i = 0; nl > 1 && i < plan.groups.size(); ++i)
-      if (!group_tuned(ctx, plan.groups[i], *hp, env.f32)) nl = 1;
-    if (nl > 1 && !ensure_lanes(ctx, nl)) nl = 1;
-    if (nl == 1) {
-      for (const Group& g : plan.groups) {
-        const int r = run_group(g, env, table + g.table_base, descs.data() + g.table_base);
-        if (r != MUON_OK) return r;
-      }
-      return MUON_OK;
-    }
-    MUON_HIP(hipEventRecord(ctx->lane_fork, env.st));
-    for (int l = 0; l < nl - 1; ++l) MUON_HIP(hipStreamWaitEvent(ctx->lanes[l], ctx->lane_fork, 0));
-    std::vector<double> load(nl, 0.0);
-    int r = MUON_OK;
-    for (const Group& g : plan.groups) {
-      const int l = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
-      load[l] += g.work;
-      StepEnv le = env;
-      if (l > 0) le.st = ctx->lanes[l - 1];
-      r = run_group(g, le, table + g.table_base, descs.data() + g.table_base);
-      if (r != MUON_OK) break;
-    }
-    // The caller's stream waits for every lane, also after a failed launch, so nothing
-    // the step enqueued outlives the caller's view of the stream.
-    for (int l = 0; l < nl - 1; ++l) {
-      if (hipEventRecord(ctx->lane_join[l], ctx->lanes[l]) != hipSuccess ||
-          hipStreamWaitEvent(env.st, ctx->lane_join[l], 0) != hipSuccess)
-        r = MUON_ERR_HIP;
-    }
-    return r;
+    void* ptr = scratch_ptr(ctx->device);
+    if (!ptr) return MUON_ERR_HIP;
+    return step_impl(ctx, mats, count, hp, ptr, kStaticScratchBytes, stream, true);
   } catch (...) {
     return MUON_ERR_HIP;
   }

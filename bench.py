@@ -148,7 +148,7 @@ TRAFFIC_SOURCES = ("matrix_orthogonalising_optimizer_muon_amd/csrc/gemm.hip",
 
 def traffic_record(workload):
     """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE and WRITE_SIZE passes, scaled by
-    a copy of known size), per stage and tile configuration, as recorded in
+    a copy of known size), per stage, tile configuration and shape group, as recorded in
     profiles/muon_step_<workload>.md; None when there is no record or the kernel sources
     changed since it was taken."""
     import hashlib
@@ -359,6 +359,20 @@ def summarise(w, r, args):
     }
 
 
+def add_traffic(roofline, workload, dom):
+    """roofline["traffic"]: HBM bytes per launch of the dominant kernel from the committed
+    counter record of the workload (null when there is none for this stage, tile and group,
+    or the kernel sources changed since it was taken)."""
+    rec = traffic_record(workload)
+    st = rec["kernels"].get(f"{dom['stage']}/{dom['tile']}/{dom['m']}x{dom['n']}x{dom['count']}") if rec else None
+    if st is not None:
+        roofline["traffic"] = st["fetch_bytes"] + st["write_bytes"]
+        roofline["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
+        roofline["traffic_kernel"] = st["kernel"]
+        if "trace_avg_us" in st:
+            roofline["rocprof_avg_us"] = st["trace_avg_us"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -403,14 +417,7 @@ def main():
                    "plan": r["plans"]},
         **sm,
     }
-    rec = traffic_record(w.name)
-    st = rec["kernels"].get(f"{dom['stage']}/{dom['tile']}") if rec else None
-    if st is not None:
-        out["roofline"]["traffic"] = st["fetch_bytes"] + st["write_bytes"]
-        out["roofline"]["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
-        out["roofline"]["traffic_kernel"] = st["kernel"]
-        if "trace_avg_us" in st:
-            out["roofline"]["rocprof_avg_us"] = st["trace_avg_us"]
+    add_traffic(out["roofline"], w.name, dom)
     also = [x for x in args.also.split(",") if x and x != w.name] if args.also else []
     if also:
         out["also"] = {}
@@ -418,7 +425,7 @@ def main():
             wa = wl.WORKLOADS[name]
             ra = run_workload(wa, args, B, torch, ctx, pctx, primary=False)
             sa = summarise(wa, ra, args)
-            sa.pop("dom")
+            add_traffic(sa["roofline"], wa.name, sa.pop("dom"))
             out["also"][name] = {"ms_per_step": round(ra["ms"], 4),
                                  "step_ms_p10_p50_p90": [round(x, 4) for x in ra["pct"]],
                                  "plan": ra["plans"],

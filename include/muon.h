@@ -195,6 +195,22 @@ int muon_workspace_size(muon_ctx *ctx, const muon_matrix *mats, int count,
 int muon_step(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hparams *hp,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Init-time profiling (DMuon summary, section 2.3: at initialisation the time of every
+ * distinct matrix shape is measured for several batch sizes and kernel schemes; section
+ * 2.4: the chosen kernel configurations are cached and reused): runs the list's update
+ * twice on synthetic data held in the workspace, measuring the tile configuration of every
+ * stage not measured yet (as muon_step's first call would, but before any training step),
+ * then times one more such run on `stream` and stores its duration in *ms (may be null).
+ * Synthetic run: the momentum stages are replaced by a seeded iterate of unit Frobenius norm
+ * (no G or M traffic) and the last product writes the workspace instead of W (no W
+ * traffic), so *ms is the Newton-Schulz part of the step. W, G and M are neither read nor
+ * written: their pointers may be null; rows and cols are used. The workspace is as for
+ * muon_step (muon_workspace_size bytes). Synchronises the stream; afterwards muon_step on
+ * the same shapes makes no host synchronisation and runs independent shape groups
+ * concurrently from its first call. Errors as muon_step. */
+int muon_prepare(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hparams *hp,
+                 void *workspace, size_t workspace_bytes, void *stream, double *ms);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): the same update as muon_step, with the
  * scratch space in a library-owned device array of MUON_STATIC_SCRATCH_BYTES instead of a
@@ -303,6 +319,45 @@ void muon_adamw_hparams_default(muon_adamw_hparams *hp);
  * MUON_ERR_HIP. */
 int muon_adamw_step(muon_ctx *ctx, const muon_adamw_tensor *tensors, int count,
                     const muon_adamw_hparams *hp, void *stream);
+
+/* ---- Owner assignment: which rank updates which matrix ----
+ * DMuon summary (gist.science), section 2.3 (compute-aware load balancing): the update
+ * cost varies strongly with the matrix shape, so each matrix is given one owner rank to
+ * minimise the predicted makespan (the largest per-rank load), from the measured time of
+ * several batch sizes per distinct shape, by an exact optimisation with a greedy fallback
+ * for large search spaces; DMuon announcement (agentren.cn), improvement 3. Host-only: no
+ * context and no device are needed.
+ *
+ * Cost model: a rank owning k matrices of one shape updates them in c(k) ms, read off the
+ * shape's measured points (batch[i], ms[i]): c(0) = 0, linear from the origin to the first
+ * point and between points, past the last point extended with the last segment's slope
+ * (the single point's mean rate when n_points == 1). A rank's load is the sum of c over
+ * its shapes. */
+#define MUON_MAX_COST_POINTS 16
+#define MUON_MAX_PLAN_RANKS 4096
+#define MUON_PLAN_GREEDY 1u            /* skip the exact search */
+#define MUON_PLAN_DEFAULT_NODES 2000000 /* search nodes when max_nodes == 0 */
+typedef struct muon_shape_cost {
+  int32_t n_points;                     /* 1..MUON_MAX_COST_POINTS */
+  int32_t batch[MUON_MAX_COST_POINTS];  /* strictly increasing batch sizes, each >= 1 */
+  double ms[MUON_MAX_COST_POINTS];      /* measured time of one update of batch[i] matrices,
+                                           finite, >= 0 */
+} muon_shape_cost;
+
+/* Owners for `count` matrices, matrix i being of shape shape_of[i] (0..n_shapes-1), over
+ * `ranks` ranks (1..MUON_MAX_PLAN_RANKS). The greedy plan (shapes by decreasing per-matrix
+ * cost, each matrix to the rank whose load grows least, then single-matrix moves off the
+ * most loaded rank while the makespan drops) starts a branch-and-bound search over the
+ * per-shape counts of every rank (skipped with MUON_PLAN_GREEDY) that stops after
+ * max_nodes nodes (0: MUON_PLAN_DEFAULT_NODES). Outputs: owner[i] in 0..ranks-1 (the
+ * matrices of one shape dealt in list order, each to the rank with the largest share of
+ * its count still open); rank_ms[r] (may be null) the predicted load of rank r;
+ * *makespan_ms (may be null) the largest of them; *optimal (may be null) 1 when the search
+ * completed, so the makespan is the least any assignment reaches under the cost model,
+ * else 0. Arrays are host memory. MUON_ERR_ARG on a bad argument (nothing written). */
+int muon_owner_plan(const int32_t *shape_of, int count, const muon_shape_cost *shapes, int n_shapes,
+                    int ranks, uint32_t flags, int64_t max_nodes, int32_t *owner, double *rank_ms,
+                    double *makespan_ms, int32_t *optimal);
 
 /* Static, human-readable text for a status code. */
 const char *muon_status_str(int status);

@@ -92,7 +92,23 @@ class muon_adamw_hparams(ctypes.Structure):
                 ("w_dtype", ctypes.c_int32), ("g_dtype", ctypes.c_int32)]
 
 
+MUON_MAX_COST_POINTS = 16
+MUON_MAX_PLAN_RANKS = 4096
+MUON_PLAN_GREEDY = 1
+MUON_PLAN_DEFAULT_NODES = 2000000
+
+
+class muon_shape_cost(ctypes.Structure):
+    _fields_ = [("n_points", ctypes.c_int32), ("batch", ctypes.c_int32 * MUON_MAX_COST_POINTS),
+                ("ms", ctypes.c_double * MUON_MAX_COST_POINTS)]
+
+
 _P = ctypes.c_void_p
+_lib.muon_owner_plan.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int, ctypes.POINTER(muon_shape_cost),
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_int64,
+                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
+_lib.muon_owner_plan.restype = ctypes.c_int
 _lib.muon_hparams_default.argtypes = [ctypes.POINTER(muon_hparams)]
 _lib.muon_hparams_default.restype = None
 _lib.muon_init.argtypes = [ctypes.POINTER(_P), ctypes.c_int, ctypes.c_uint32]
@@ -103,6 +119,9 @@ _lib.muon_workspace_size.restype = ctypes.c_int
 _lib.muon_step.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int,
                            ctypes.POINTER(muon_hparams), _P, ctypes.c_size_t, _P]
 _lib.muon_step.restype = ctypes.c_int
+_lib.muon_prepare.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int, ctypes.POINTER(muon_hparams),
+                              _P, ctypes.c_size_t, _P, ctypes.POINTER(ctypes.c_double)]
+_lib.muon_prepare.restype = ctypes.c_int
 _lib.muon_step_static.argtypes = [_P, ctypes.POINTER(muon_matrix), ctypes.c_int,
                                   ctypes.POINTER(muon_hparams), _P]
 _lib.muon_step_static.restype = ctypes.c_int
@@ -252,6 +271,21 @@ def muon_step(ctx, mats, hp: muon_hparams, workspace_ptr: int, workspace_bytes: 
                           ctypes.c_size_t(workspace_bytes), ctypes.c_void_p(stream_ptr))
 
 
+def muon_prepare(ctx, mats, hp: muon_hparams, workspace_ptr: int, workspace_bytes: int,
+                 stream_ptr: int | None = None, count: int | None = None) -> float:
+    """Measure the tiles of every stage of the list ahead of the first step (synthetic data in
+    the workspace; W, G, M untouched) and return the time of one synthetic run in ms."""
+    arr = mats if isinstance(mats, ctypes.Array) else matrix_list(mats)
+    n = len(mats) if count is None else count
+    if stream_ptr is None:
+        stream_ptr = torch.cuda.current_stream().cuda_stream
+    ms = ctypes.c_double()
+    check(_lib.muon_prepare(ctx, arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace_ptr),
+                            ctypes.c_size_t(workspace_bytes), ctypes.c_void_p(stream_ptr), ctypes.byref(ms)),
+          "muon_prepare")
+    return ms.value
+
+
 def muon_step_static(ctx, mats, hp: muon_hparams, stream_ptr: int | None = None,
                      count: int | None = None) -> int:
     """Enqueue one update over the library's static scratch (no workspace); returns the
@@ -346,14 +380,43 @@ def muon_adamw_step(ctx, tensors, hp: muon_adamw_hparams, stream_ptr=None, count
     return _lib.muon_adamw_step(ctx, arr, n, ctypes.byref(hp), stream_ptr)
 
 
+def shape_cost(points) -> muon_shape_cost:
+    """A ``muon_shape_cost`` from [(batch, ms), ...] measured points."""
+    c = muon_shape_cost()
+    c.n_points = len(points)
+    for i, (b, ms) in enumerate(points):
+        c.batch[i] = int(b)
+        c.ms[i] = float(ms)
+    return c
+
+
+def muon_owner_plan(shape_of, costs, ranks: int, greedy: bool = False, max_nodes: int = 0) -> dict:
+    """Owner map of matrices (shape ids ``shape_of``) over ``ranks`` ranks from per-shape
+    measured costs (a list of [(batch, ms), ...] or ``muon_shape_cost``). Returns a dict with
+    ``owner`` (list), ``rank_ms`` (list), ``makespan_ms`` and ``optimal``."""
+    n = len(shape_of)
+    so = (ctypes.c_int32 * max(n, 1))(*shape_of)
+    cs = (muon_shape_cost * max(len(costs), 1))(
+        *[c if isinstance(c, muon_shape_cost) else shape_cost(c) for c in costs])
+    owner = (ctypes.c_int32 * max(n, 1))()
+    rank_ms = (ctypes.c_double * max(ranks, 1))()
+    mk = ctypes.c_double()
+    opt = ctypes.c_int32()
+    check(_lib.muon_owner_plan(so, n, cs, len(costs), int(ranks), MUON_PLAN_GREEDY if greedy else 0,
+                               int(max_nodes), owner, rank_ms, ctypes.byref(mk), ctypes.byref(opt)),
+          "muon_owner_plan")
+    return {"owner": list(owner[:n]), "rank_ms": list(rank_ms[:ranks]), "makespan_ms": mk.value,
+            "optimal": bool(opt.value)}
+
+
 def muon_destroy(ctx) -> int:
     return _lib.muon_destroy(ctx)
 
 
 def exported_symbols() -> list:
     """Names of the C entry points this binding resolved (each must exist in the .so)."""
-    return [n for n in ("muon_hparams_default", "muon_init", "muon_workspace_size", "muon_step", "muon_step_static",
+    return [n for n in ("muon_hparams_default", "muon_init", "muon_workspace_size", "muon_step", "muon_step_static", "muon_prepare",
                         "muon_plan_info", "muon_debug_gemm", "muon_profile_read", "muon_tune_save",
                         "muon_tune_load", "muon_adamw_hparams_default", "muon_adamw_step",
-                        "muon_destroy", "muon_status_str")
+                        "muon_destroy", "muon_status_str", "muon_owner_plan")
             if hasattr(_lib, n)]

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "muon_amd")
 LIB = os.path.join(PKG, "libmuon_amd.so")
-SOURCES = ["api.cpp", "gemm.hip", "elementwise.hip", "small.hip", "adamw.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "elementwise.hip", "small.hip", "adamw.hip", "planner.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -302,6 +302,9 @@ struct StepEnv {
   // muon_step_static: no tile measurement (cached choices or the static ones), no
   // profiler events, one stream; nothing is created or allocated.
   bool no_alloc = false;
+  // muon_prepare: the momentum stages are replaced by a seeded stand-in iterate (launch_dry_x)
+  // and the last product writes the workspace instead of W, so W, G, M are not touched.
+  bool dry = false;
 };
 
 // One stage name per kernel: "momentum_norm" the first pass over G and M (partial sums of
@@ -644,6 +647,7 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
     sp.n_segments = hp.n_segments;
     for (int k = 0; k < hp.n_segments; ++k) sp.segments[k] = hp.segments[k];
     sp.g_bf16 = hp.g_dtype == MUON_BF16; sp.m_bf16 = hp.m_dtype == MUON_BF16; sp.w_bf16 = hp.w_dtype == MUON_BF16;
+    sp.dry = env.dry ? 1 : 0;
     const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;
     const double wb = hp.w_dtype == MUON_BF16 ? 2.0 : 4.0;
     StageTimer tm(timer_ctx(env), env.st, ST_SINGLE_WG, g.m, g.n, count, dense_flops(g.m, g.n, g.mode, hp) * count,
@@ -687,22 +691,26 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
   const double gb = hp.g_dtype == MUON_BF16 ? 2.0 : 4.0, mb = hp.m_dtype == MUON_BF16 ? 2.0 : 4.0;
   const double xb = f32 ? 4.0 : 2.0;
   const double elems = static_cast<double>(count) * g.m * g.n;
-  {
-    // algorithmic bytes: G and M read
-    StageTimer tm(timer_ctx(env), env.st, ST_MOMENTUM_NORM, g.m, g.n, count, 0.0, elems * (gb + mb));
-    MUON_HIP(launch_momentum_norm(mp, env.st));
-    tm.done();
-  }
-  {
-    StageTimer tm(timer_ctx(env), env.st, ST_FINALIZE, g.m, g.n, count, 0.0, 4.0 * count * g.norm_blocks);
-    MUON_HIP(launch_norm_finalize(mp.partials, g.norm_blocks, count, hp.eps, s, env.st));
-    tm.done();
-  }
-  {
-    // algorithmic bytes: G and M read, M' written, X0 written in two layouts
-    StageTimer tm(timer_ctx(env), env.st, ST_MOMENTUM, g.m, g.n, count, 0.0, elems * (gb + 2.0 * mb + 2.0 * xb));
-    MUON_HIP(launch_momentum_x(mp, env.st));
-    tm.done();
+  if (env.dry) {
+    MUON_HIP(launch_dry_x(mp, env.st));
+  } else {
+    {
+      // algorithmic bytes: G and M read
+      StageTimer tm(timer_ctx(env), env.st, ST_MOMENTUM_NORM, g.m, g.n, count, 0.0, elems * (gb + mb));
+      MUON_HIP(launch_momentum_norm(mp, env.st));
+      tm.done();
+    }
+    {
+      StageTimer tm(timer_ctx(env), env.st, ST_FINALIZE, g.m, g.n, count, 0.0, 4.0 * count * g.norm_blocks);
+      MUON_HIP(launch_norm_finalize(mp.partials, g.norm_blocks, count, hp.eps, s, env.st));
+      tm.done();
+    }
+    {
+      // algorithmic bytes: G and M read, M' written, X0 written in two layouts
+      StageTimer tm(timer_ctx(env), env.st, ST_MOMENTUM, g.m, g.n, count, 0.0, elems * (gb + 2.0 * mb + 2.0 * xb));
+      MUON_HIP(launch_momentum_x(mp, env.st));
+      tm.done();
+    }
   }
 
   int cur = 0;
@@ -716,7 +724,7 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
       MUON_HIP(syrk(g, env, X, A, e * ixs * ixs));
       MUON_HIP(square(g, env, A, A, A, B, c1, b1, 0.0f));           // B = b A + c A^2
       // X' = a X + B X  (X taken from its transposed copy, which carries xs)
-      MUON_HIP(apply(g, env, B, XT[cur], X, XT[cur ^ 1], ixs, a * ixs, xs, true, last, table));
+      MUON_HIP(apply(g, env, B, XT[cur], X, XT[cur ^ 1], ixs, a * ixs, xs, true, last && !env.dry, table));
       cur ^= 1;
     }
   } else {
@@ -735,7 +743,7 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
         MUON_HIP(square(g, env, T1, Q, nullptr, T2, 1.0f, 0.0f, 0.0f));  // Q <- P Q
         std::swap(Q, T2);
       }
-      MUON_HIP(apply(g, env, Q, XT[cur], X, XT[cur ^ 1], ixs, 0.0f, xs, false, last, table));
+      MUON_HIP(apply(g, env, Q, XT[cur], X, XT[cur ^ 1], ixs, 0.0f, xs, false, last && !env.dry, table));
       cur ^= 1;
     }
   }
@@ -783,14 +791,14 @@ void* scratch_ptr(int device) {
 }
 
 int step_impl(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams* hp, void* workspace,
-              size_t workspace_bytes, void* stream, bool no_alloc) {
+              size_t workspace_bytes, void* stream, bool no_alloc, bool dry = false) {
   {
     if (!ctx || count < 0 || (count > 0 && !mats)) return MUON_ERR_ARG;
     const int rc = validate_hparams(hp);
     if (rc != MUON_OK) return rc;
     if (count == 0) return MUON_OK;
     Plan plan;
-    const int pc = build_plan(ctx, mats, count, *hp, true, plan);
+    const int pc = build_plan(ctx, mats, count, *hp, !dry, plan);
     if (pc != MUON_OK) return pc;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 ||
         workspace_bytes < plan.bytes)
@@ -799,7 +807,7 @@ int step_impl(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
     DeviceGuard dg(ctx->device);
     if (!dg.ok) return MUON_ERR_HIP;
     StepEnv env{static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
-                hp->ns_dtype == MUON_F32, hp, ctx, no_alloc};
+                hp->ns_dtype == MUON_F32, hp, ctx, no_alloc, dry};
     MatDesc* table = reinterpret_cast<MatDesc*>(env.ws + plan.off_table);
     // Descriptor table, ordered by group, written by small kernels (no host sync).
     std::vector<MatDesc> descs(count);
@@ -952,6 +960,47 @@ int muon_step(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
               void* workspace, size_t workspace_bytes, void* stream) {
   try {
     return step_impl(ctx, mats, count, hp, workspace, workspace_bytes, stream, false);
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+int muon_prepare(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams* hp, void* workspace,
+                 size_t workspace_bytes, void* stream, double* ms) {
+  try {
+    if (ms) *ms = 0.0;
+    if (!ctx || count < 0 || (count > 0 && !mats)) return MUON_ERR_ARG;
+    const int rc = validate_hparams(hp);
+    if (rc != MUON_OK) return rc;
+    if (count == 0) return MUON_OK;
+    {
+      Plan plan;
+      const int pc = build_plan(ctx, mats, count, *hp, false, plan);
+      if (pc != MUON_OK) return pc;
+      if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < plan.bytes)
+        return MUON_ERR_WORKSPACE;
+    }
+    if (ctx->device < 0) return MUON_ERR_DEVICE;
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return MUON_ERR_HIP;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    // First dry run: every stage whose tiles are not cached measures them (the plan may then
+    // change, e.g. MUON_NS_AUTO's plain / Gram choice, so a second run measures the rest).
+    for (int pass = 0; pass < 2; ++pass) {
+      const int r = step_impl(ctx, mats, count, hp, workspace, workspace_bytes, stream, false, true);
+      if (r != MUON_OK) return r;
+    }
+    for (int i = 0; i < 2; ++i)
+      if (!ctx->tune_ev[i] && hipEventCreate(&ctx->tune_ev[i]) != hipSuccess) return MUON_ERR_HIP;
+    MUON_HIP(hipEventRecord(ctx->tune_ev[0], st));
+    const int r = step_impl(ctx, mats, count, hp, workspace, workspace_bytes, stream, false, true);
+    if (r != MUON_OK) return r;
+    MUON_HIP(hipEventRecord(ctx->tune_ev[1], st));
+    MUON_HIP(hipEventSynchronize(ctx->tune_ev[1]));
+    float t = 0.0f;
+    MUON_HIP(hipEventElapsedTime(&t, ctx->tune_ev[0], ctx->tune_ev[1]));
+    if (ms) *ms = t;
+    return MUON_OK;
   } catch (...) {
     return MUON_ERR_HIP;
   }

@@ -240,6 +240,33 @@ __global__ __launch_bounds__(kThreads) void momentum_x_kernel(const MomentumPara
   }
 }
 
+// Dry-run iterate: each thread writes 8 consecutive elements of X (row-major) and 8 of X^T,
+// computing every value from its canonical position, so both layouts agree exactly.
+__global__ __launch_bounds__(kThreads) void dry_x_kernel(const MomentumParams p) {
+  const int mat = blockIdx.y;
+  const int t = blockIdx.x;
+  const int ti = t / p.tiles_n, tj = t % p.tiles_n;
+  const int i0 = ti * kTile, j0 = tj * kTile;
+  const int tid = threadIdx.x;
+  const int cr = tid >> 3, cc = (tid & 7) * 8;
+  const float sc = p.xscale * sqrtf(3.0f / (static_cast<float>(p.m) * static_cast<float>(p.n)));
+  const int64_t base = static_cast<int64_t>(mat) * p.sX;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int lr = cr + pass * 32;
+    float v[8], w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = i0 + lr, c = j0 + cc + e;            // X row i0 + lr
+      v[e] = (r < p.m && c < p.n) ? sc * dry_u(mat, r, c) : 0.0f;
+      const int r2 = i0 + cc + e, c2 = j0 + lr;          // X^T row j0 + lr
+      w[e] = (r2 < p.m && c2 < p.n) ? sc * dry_u(mat, r2, c2) : 0.0f;
+    }
+    store_x8(p.X, base + static_cast<int64_t>(i0 + lr) * p.Np + j0 + cc, p.x_f16, v);
+    store_x8(p.XT, base + static_cast<int64_t>(j0 + lr) * p.Mp + i0 + cc, p.x_f16, w);
+  }
+}
+
 constexpr int kFinThreads = 1024;
 
 __global__ __launch_bounds__(kFinThreads) void norm_finalize_kernel(const float* partials, int per_matrix,
@@ -299,6 +326,12 @@ hipError_t launch_norm_finalize(const float* partials, int per_matrix, int count
                                 float* s, hipStream_t st) {
   if (count <= 0) return hipSuccess;
   hipLaunchKernelGGL(norm_finalize_kernel, dim3(count), dim3(kFinThreads), 0, st, partials, per_matrix, eps, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dry_x(const MomentumParams& p, hipStream_t st) {
+  if (p.count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dry_x_kernel, dim3(p.tiles_m * p.tiles_n, p.count), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

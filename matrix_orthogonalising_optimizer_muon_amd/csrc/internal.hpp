@@ -141,6 +141,17 @@ hipError_t launch_momentum_norm(const MomentumParams& p, hipStream_t st);
 hipError_t launch_momentum_x(const MomentumParams& p, hipStream_t st);
 constexpr int kNormBlock = 4096;  // stored elements per partial sum
 
+// Dry runs (muon_prepare): a seeded stand-in for the momentum output, U(i, r, c) =
+// dry_u(i, r, c) uniform in [-1, 1) for the canonical element (r, c) of matrix i.
+__host__ __device__ inline float dry_u(uint32_t mat, uint32_t r, uint32_t c) {
+  uint32_t h = mat * 0x9E3779B9u ^ (r * 0x85EBCA6Bu + 0x27D4EB2Fu) ^ (c * 0xC2B2AE35u + 0x165667B1u);
+  h ^= h >> 16; h *= 0x7FEB352Du; h ^= h >> 15; h *= 0x846CA68Bu; h ^= h >> 16;
+  return static_cast<float>(h >> 8) * (2.0f / 16777216.0f) - 1.0f;
+}
+// X0 = xscale * sqrt(3 / (m n)) * dry_u (unit Frobenius norm in expectation) in both layouts,
+// zero padding; the partials, s and M are not touched.
+hipError_t launch_dry_x(const MomentumParams& p, hipStream_t st);
+
 // s[i] = 1 / (sqrt(sum_j partials[i][j]) + eps), fixed-order fp64 reduction.
 hipError_t launch_norm_finalize(const float* partials, int per_matrix, int count, float eps,
                                 float* s, hipStream_t st);
@@ -163,6 +174,9 @@ struct SmallParams {
   int32_t n_segments;
   int32_t segments[8];
   int32_t g_bf16, m_bf16, w_bf16;
+  // Dry run (muon_prepare): U comes from dry_u() instead of G and M, nothing is stored to
+  // M or W (the last product writes the iterate to the workspace instead).
+  int32_t dry;
 };
 hipError_t launch_small_ns(const SmallParams& p, hipStream_t st);
 constexpr int kSmallMaxElems = 64 * 1024;  // padded m' n' the single-workgroup kernel takes

@@ -194,11 +194,27 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
       u[k] = p.nesterov ? g[k] + p.mu * mn[k] : mn[k];
     }
   };
-  float sq = 0.0f;
-  for (int gi = tid; gi < rows * gpr; gi += NT) {
-    float g[8], m[8], mn[8], u[8];
+  // U of stored group gi: from G and M, or in a dry run (muon_prepare) the seeded stand-in
+  // (G and M are then neither read nor written).
+  auto momentum_u = [&](int gi, float (&mn)[8], float (&u)[8]) {
+    if (p.dry) {
+      const int sr = gi / gpr, sc0 = (gi % gpr) * 8;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = d.transposed ? sc0 + k : sr, c = d.transposed ? sr : sc0 + k;
+        u[k] = sc0 + k < cols ? dry_u(mat, r, c) : 0.0f;
+        mn[k] = 0.0f;
+      }
+      return;
+    }
+    float g[8], m[8];
     load_gm(gi, g, m);
     momentum8(g, m, mn, u);
+  };
+  float sq = 0.0f;
+  for (int gi = tid; gi < rows * gpr; gi += NT) {
+    float mn[8], u[8];
+    momentum_u(gi, mn, u);
 #pragma unroll
     for (int k = 0; k < 8; ++k) sq += u[k] * u[k];   // zero past the row end
   }
@@ -211,15 +227,14 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
   const float s = static_cast<float>(1.0 / (sqrt(red[0]) + static_cast<double>(p.eps)));
   const float xsc = p.xs * s;
   for (int gi = tid; gi < rows * gpr; gi += NT) {
-    float g[8], m[8], mn[8], u[8];
-    load_gm(gi, g, m);
-    momentum8(g, m, mn, u);
+    float mn[8], u[8];
+    momentum_u(gi, mn, u);
     const int sr = gi / gpr, sc0 = (gi % gpr) * 8;
     const int64_t base = static_cast<int64_t>(sr) * cols + sc0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       if (sc0 + k >= cols) continue;
-      store_elem(d.M, base + k, mn[k], p.m_bf16);
+      if (!p.dry) store_elem(d.M, base + k, mn[k], p.m_bf16);
       const int r = d.transposed ? sc0 + k : sr, c = d.transposed ? sr : sc0 + k;
       U[r * Np + c] = f32_to_f16(xsc * u[k]);
     }
@@ -420,7 +435,7 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
         for (int e = 0; e < 16; ++e) o[e] = f16_to_f32(X[static_cast<int64_t>(rb + (e >> 2) * 8 + (e & 3)) * Np + c]);
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[e] = v[e] + p.a * o[e];
-        if (last) update(rb, c, o);
+        if (last && !p.dry) update(rb, c, o);
         else store_x(xtn, rb, c, o);
       });
       cur ^= 1;
@@ -445,7 +460,7 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
     }
     u16* xtn = XT[cur ^ 1];
     apply(Q, XT[cur], [&](int rb, int c, const f32x16& v) {
-      if (last) update(rb, c, v);
+      if (last && !p.dry) update(rb, c, v);
       else store_x(xtn, rb, c, v);
     });
     cur ^= 1;

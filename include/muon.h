@@ -271,6 +271,30 @@ int muon_debug_gemm(muon_ctx *ctx, int kind, int ns_dtype, int tile, int64_t M, 
                     int64_t K, const void *A, const void *B, const void *E, void *C, void *C2,
                     float alpha, float beta, float gamma, float oscale, void *stream);
 
+/* Test-only entry point: one element-wise stage of the pipeline, or the weight update, on a
+ * single matrix (W, G, M as in muon_step; hp as in muon_step), enqueued on `stream`:
+ *   MUON_STAGE_NORM:    out (device, 1 fp32) = 1 / (||U||_F + eps), U = G + mu (mu M + G)
+ *                       (or mu M + G without Nesterov); G and M are only read.
+ *   MUON_STAGE_ITERATE: M <- mu M + G, and the normalised iterate times *scale (a power of
+ *                       two chosen by the library, 1 on the fp32 path) in the canonical
+ *                       orientation: out = scale X0 (Mp x Np row-major) and out2 = its
+ *                       transpose (Np x Mp), Mp, Np the canonical sizes rounded up to 64,
+ *                       zero outside m' x n'; fp16 for ns_dtype MUON_BF16, else fp32.
+ *   MUON_STAGE_UPDATE:  W <- W (1 - lr wd) - lr O with O = Q X, Q = in (Mp x Mp) and out2
+ *                       holding scale X^T (Np x Mp) as MUON_STAGE_ITERATE writes it, both in
+ *                       the iterate's type; O's canonical m' x n' block goes to W through the
+ *                       orientation map (transposed for rows > cols); out must be non-null
+ *                       (unused). G and M may be null.
+ * *scale (host, may be null) receives the iterate's scale. The workspace needs 512 bytes
+ * plus 4 per 4096 elements of the matrix (rounded up to 256), 256-byte aligned. Validation
+ * as muon_step (MUON_ERR_ARG also for a null operand the stage uses). */
+#define MUON_STAGE_NORM 0
+#define MUON_STAGE_ITERATE 1
+#define MUON_STAGE_UPDATE 2
+int muon_debug_stage(muon_ctx *ctx, int stage, const muon_matrix *mat, const muon_hparams *hp,
+                     const void *in, void *out, void *out2, float *scale, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 /* Profiler read-out for a context created with MUON_FLAG_PROFILE: waits for the last
  * recorded launch, aggregates all launches recorded since the previous read by (stage,
  * shape, batch, tile) in first-seen order into out[0..capacity), stores the number of entries

@@ -134,6 +134,10 @@ _lib.muon_debug_gemm.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, c
                                  ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_float,
                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, _P]
 _lib.muon_debug_gemm.restype = ctypes.c_int
+_lib.muon_debug_stage.argtypes = [_P, ctypes.c_int, ctypes.POINTER(muon_matrix), ctypes.POINTER(muon_hparams),
+                                  _P, _P, _P, ctypes.POINTER(ctypes.c_float), _P, ctypes.c_size_t, _P]
+_lib.muon_debug_stage.restype = ctypes.c_int
+MUON_STAGE_NORM, MUON_STAGE_ITERATE, MUON_STAGE_UPDATE = 0, 1, 2
 _lib.muon_profile_read.argtypes = [_P, ctypes.POINTER(muon_profile_entry), ctypes.c_int,
                                    ctypes.POINTER(ctypes.c_int)]
 _lib.muon_profile_read.restype = ctypes.c_int
@@ -315,6 +319,23 @@ def muon_debug_gemm(ctx, kind, ns_dtype, tile, M, N, K, A, B, E, C, C2=None, alp
                                 ctypes.c_void_p(stream_ptr))
 
 
+def muon_debug_stage(ctx, stage: int, mat, hp: muon_hparams, inp, out, out2, workspace,
+                     stream_ptr=None) -> tuple:
+    """One stage on one matrix (test-only). ``mat`` is (W, G, M) tensors (None allowed where
+    the stage does not use them) plus rows, cols; the rest are tensors or None. Returns
+    (status, scale)."""
+    W, G, M, rows, cols = mat
+    ptr = lambda t: None if t is None else t.data_ptr()
+    m = muon_matrix(ptr(W), ptr(G), ptr(M), rows, cols)
+    sc = ctypes.c_float()
+    if stream_ptr is None:
+        stream_ptr = torch.cuda.current_stream().cuda_stream
+    rc = _lib.muon_debug_stage(ctx, int(stage), ctypes.byref(m), ctypes.byref(hp), ptr(inp), ptr(out), ptr(out2),
+                               ctypes.byref(sc), ptr(workspace), workspace.numel() * workspace.element_size(),
+                               ctypes.c_void_p(stream_ptr))
+    return rc, sc.value
+
+
 def muon_profile_read(ctx, capacity: int = 256) -> list:
     """Aggregated per-stage launch timings since the last read, as dicts."""
     buf = (muon_profile_entry * capacity)()
@@ -416,7 +437,7 @@ def muon_destroy(ctx) -> int:
 def exported_symbols() -> list:
     """Names of the C entry points this binding resolved (each must exist in the .so)."""
     return [n for n in ("muon_hparams_default", "muon_init", "muon_workspace_size", "muon_step", "muon_step_static", "muon_prepare",
-                        "muon_plan_info", "muon_debug_gemm", "muon_profile_read", "muon_tune_save",
+                        "muon_plan_info", "muon_debug_gemm", "muon_debug_stage", "muon_profile_read", "muon_tune_save",
                         "muon_tune_load", "muon_adamw_hparams_default", "muon_adamw_step",
                         "muon_destroy", "muon_status_str", "muon_owner_plan")
             if hasattr(_lib, n)]

@@ -1152,6 +1152,80 @@ int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon
   }
 }
 
+int muon_debug_stage(muon_ctx* ctx, int stage, const muon_matrix* mat, const muon_hparams* hp, const void* in,
+                     void* out, void* out2, float* scale, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!ctx || !mat || stage < MUON_STAGE_NORM || stage > MUON_STAGE_UPDATE) return MUON_ERR_ARG;
+    const int rc = validate_hparams(hp);
+    if (rc != MUON_OK) return rc;
+    const int vm = validate_matrix(*mat, false);
+    if (vm != MUON_OK) return vm;
+    const bool need_gm = stage != MUON_STAGE_UPDATE, need_w = stage == MUON_STAGE_UPDATE;
+    if ((need_gm && (!mat->G || !mat->M)) || (need_w && (!mat->W || !in)) || !out || (stage != MUON_STAGE_NORM && !out2))
+      return MUON_ERR_ARG;
+    Group g;
+    g.m = std::min(mat->rows, mat->cols); g.n = std::max(mat->rows, mat->cols);
+    g.Mp = round_up(g.m, kPad); g.Np = round_up(g.n, kPad);
+    g.members = {0};
+    g.has_tall = mat->rows > mat->cols;
+    g.mom_tiles_m = static_cast<int>(g.Mp / 64); g.mom_tiles_n = static_cast<int>(g.Np / 64);
+    g.norm_blocks = static_cast<int>((g.m * g.n + kNormBlock - 1) / kNormBlock);
+    g.stride_x = g.Mp * g.Np; g.stride_sq = g.Mp * g.Mp;
+    const bool f32 = hp->ns_dtype == MUON_F32;
+    g.tile_ap = heuristic_apply(g.Mp, g.Np, 1, ctx->cu_count, f32);
+    g.hs = *hp;
+    // workspace: descriptor, partials, s
+    const size_t off_part = kAlign, off_s = align_up(off_part + sizeof(float) * g.norm_blocks);
+    const size_t need = off_s + kAlign;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < need)
+      return MUON_ERR_WORKSPACE;
+    if (ctx->device < 0) return MUON_ERR_DEVICE;
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return MUON_ERR_HIP;
+    char* ws = static_cast<char*>(workspace);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    MatDesc* table = reinterpret_cast<MatDesc*>(ws);
+    TableChunk c;
+    std::memset(&c, 0, sizeof(c));
+    c.n = 1;
+    c.d[0].W = mat->W; c.d[0].G = mat->G; c.d[0].M = mat->M;
+    c.d[0].rows = mat->rows; c.d[0].cols = mat->cols; c.d[0].transposed = mat->rows > mat->cols ? 1 : 0;
+    MUON_HIP(launch_write_table(c, table, st));
+    const float xs = f32 ? 1.0f : pow2_near(std::sqrt(static_cast<double>(g.m) * g.n), 0, 14);
+    if (scale) *scale = xs;
+    if (stage == MUON_STAGE_UPDATE) {
+      StepEnv env{ws, st, f32, hp, ctx, true, false};
+      g.off_s = off_s;
+      // O = Q X / xs from Q (in, Mp x Mp) and xs X^T (out2, Np x Mp); W updated through the
+      // orientation map (out is unused but must be non-null).
+      MUON_HIP(apply(g, env, in, out2, out, nullptr, 1.0f / xs, 0.0f, xs, false, true, table));
+      return MUON_OK;
+    }
+    MomentumParams mp;
+    std::memset(&mp, 0, sizeof(mp));
+    mp.table = table;
+    mp.X = out; mp.XT = out2;
+    mp.sX = g.stride_x;
+    mp.m = static_cast<int32_t>(g.m); mp.n = static_cast<int32_t>(g.n);
+    mp.Mp = static_cast<int32_t>(g.Mp); mp.Np = static_cast<int32_t>(g.Np);
+    mp.tiles_m = g.mom_tiles_m; mp.tiles_n = g.mom_tiles_n;
+    mp.norm_blocks = g.norm_blocks;
+    mp.count = 1;
+    mp.mu = hp->momentum; mp.nesterov = hp->nesterov;
+    mp.g_bf16 = hp->g_dtype == MUON_BF16; mp.m_bf16 = hp->m_dtype == MUON_BF16; mp.x_f16 = !f32;
+    mp.xscale = xs;
+    float* s = stage == MUON_STAGE_NORM ? static_cast<float*>(out) : reinterpret_cast<float*>(ws + off_s);
+    mp.s = s;
+    mp.partials = reinterpret_cast<float*>(ws + off_part);
+    MUON_HIP(launch_momentum_norm(mp, st));
+    MUON_HIP(launch_norm_finalize(mp.partials, g.norm_blocks, 1, hp->eps, s, st));
+    if (stage == MUON_STAGE_ITERATE) MUON_HIP(launch_momentum_x(mp, st));
+    return MUON_OK;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
 int muon_debug_gemm(muon_ctx* ctx, int kind, int ns_dtype, int tile, int64_t M, int64_t N, int64_t K,
                     const void* A, const void* B, const void* E, void* C, void* C2, float alpha,
                     float beta, float gamma, float oscale, void* stream) {

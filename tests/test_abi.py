@@ -441,3 +441,20 @@ def test_muon_update_takes_dtypes_from_tensors():
         MuonUpdate([(W, G, M), (W.float(), G, M)], device=0)
     with pytest.raises(ValueError, match="not on a GPU"):    # dtypes agree; host tensors
         MuonUpdate([(W, G, M)], device=0)
+
+
+def test_debug_stage_validation_on_host(hctx):
+    """muon_debug_stage validates its arguments before touching a device: a host-only
+    context gets MUON_ERR_DEVICE only for a valid call."""
+    m = B.muon_matrix(8, 16, 24, 64, 100)      # non-null host-side stand-ins, never dereferenced
+    hp = B.make_hparams()
+    f = ctypes.c_float()
+    assert B._lib.muon_debug_stage(hctx, 7, ctypes.byref(m), ctypes.byref(hp), None, ctypes.c_void_p(64),
+                                   None, ctypes.byref(f), ctypes.c_void_p(256), 4096, None) == B.MUON_ERR_ARG
+    assert B._lib.muon_debug_stage(hctx, 0, ctypes.byref(m), ctypes.byref(hp), None, ctypes.c_void_p(64),
+                                   None, ctypes.byref(f), ctypes.c_void_p(256), 300, None) == B.MUON_ERR_WORKSPACE
+    assert B._lib.muon_debug_stage(hctx, 0, ctypes.byref(m), ctypes.byref(hp), None, ctypes.c_void_p(64),
+                                   None, ctypes.byref(f), ctypes.c_void_p(256), 4096, None) == B.MUON_ERR_DEVICE
+    bad = B.make_hparams(momentum=2.0)
+    assert B._lib.muon_debug_stage(hctx, 0, ctypes.byref(m), ctypes.byref(bad), None, ctypes.c_void_p(64),
+                                   None, ctypes.byref(f), ctypes.c_void_p(256), 4096, None) == B.MUON_ERR_ARG

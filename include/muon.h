@@ -158,13 +158,19 @@ typedef struct muon_profile_entry {
  * (3.4445, -4.7750, 2.0315), segments 2+2+1, mode AUTO, W fp32, G and M bf16, NS bf16. */
 void muon_hparams_default(muon_hparams *hp);
 
-/* Create a context on HIP device `device`. The device must be gfx950, else
+/* Context, workspace and status calls (muon_init, muon_workspace_size, muon_destroy,
+ * muon_status_str): the pages describe the integration only as naming the participating
+ * matrices and replacing the optimizer (MuonX article, section 3.3; DMuon announcement,
+ * "three lines of code"); these calls are this library's own interface around it.
+ *
+ * Create a context on HIP device `device`. The device must be gfx950, else
  * MUON_ERR_DEVICE. device == -1 creates a host-only context (no HIP call is made; it
  * plans for a 256-CU MI355X): muon_workspace_size and muon_plan_info work, muon_step and
  * muon_debug_gemm validate their arguments and then return MUON_ERR_DEVICE.
  * `flags` is 0 or a combination of MUON_FLAG_MODEL_ONLY, MUON_FLAG_PROFILE and
  * MUON_FLAG_STAGED_ONLY. *out receives the context; it is owned by the
- * caller until muon_destroy. No device memory is allocated. */
+ * caller until muon_destroy. No device memory is allocated (the device's copy of the
+ * muon_step_static scratch array comes with the library's code, which this call looks up). */
 int muon_init(muon_ctx **out, int device, uint32_t flags);
 
 /* Bytes of device workspace muon_step needs for this list and these hyper-parameters

@@ -60,5 +60,60 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C++ front end (argument
+# validation, planning, tune-file parsing, owner planner) for the host-only tests. Device
+# code is built as usual (sanitizers apply to the host pass only); the kernels' objects of
+# the regular build are reused when they are newer than their sources.
+SAN_OBJ = os.path.join(ROOT, "_build", "asan")
+SAN_LIB = os.path.join(SAN_OBJ, "libmuon_amd_asan.so")
+SAN_SOURCES = ["api.cpp", "planner.cpp"]
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime() -> str | None:
+    """The clang AddressSanitizer runtime to preload into an uninstrumented Python."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    hits = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    hits += sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[0] if hits else None
+
+
+def build_asan(verbose: bool = False) -> str:
+    os.makedirs(SAN_OBJ, exist_ok=True)
+
+    def obj(src):
+        if src in SAN_SOURCES:
+            out = os.path.join(SAN_OBJ, os.path.splitext(src)[0] + ".o")
+            cmd = [HIPCC, *[f for f in FLAGS if f != "-O3"], "-O1", "-g", *SAN_FLAGS, "-c",
+                   os.path.join(CSRC, src), "-o", out]
+        else:
+            out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+            if os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(os.path.join(CSRC, src)):
+                return out
+            os.makedirs(OBJ, exist_ok=True)
+            cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+        return out
+
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(obj, SOURCES))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-shared-libasan", "-Xarch_host",
+           "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", *objs, "-o", SAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

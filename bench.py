@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--tune-cache", default=None,
                     help="tile-choice file: loaded before the warmup when it exists, written after "
                          "it (so that separate profiling runs use the same kernels)")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run every shape group on the launch stream (MUON_FLAG_ONE_STREAM) instead of "
+                         "up to four concurrent streams")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before warmup, copy this many MiB device-to-device once (a plain copy "
                          "kernel of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -386,7 +389,7 @@ def main():
 
     w = wl.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    ctx = B.muon_init(0)
+    ctx = B.muon_init(0, B.MUON_FLAG_ONE_STREAM if args.one_stream else 0)
     pctx = B.muon_init(0, B.MUON_FLAG_PROFILE)
     r = run_workload(w, args, B, torch, ctx, pctx, primary=True)
     sm = summarise(w, r, args)

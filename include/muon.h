@@ -58,6 +58,7 @@ extern "C" {
 #define MUON_FLAG_MODEL_ONLY 1u  /* no timed tile tuning: static tile choice only */
 #define MUON_FLAG_PROFILE 2u     /* bracket every launch with hipEvents (muon_profile_read) */
 #define MUON_FLAG_STAGED_ONLY 4u /* never use the single-workgroup kernel for small matrices */
+#define MUON_FLAG_ONE_STREAM 8u  /* run every shape group on the caller's stream, in order */
 
 typedef struct muon_ctx muon_ctx; /* opaque; owned by the library */
 
@@ -167,8 +168,8 @@ void muon_hparams_default(muon_hparams *hp);
  * MUON_ERR_DEVICE. device == -1 creates a host-only context (no HIP call is made; it
  * plans for a 256-CU MI355X): muon_workspace_size and muon_plan_info work, muon_step and
  * muon_debug_gemm validate their arguments and then return MUON_ERR_DEVICE.
- * `flags` is 0 or a combination of MUON_FLAG_MODEL_ONLY, MUON_FLAG_PROFILE and
- * MUON_FLAG_STAGED_ONLY. *out receives the context; it is owned by the
+ * `flags` is 0 or a combination of MUON_FLAG_MODEL_ONLY, MUON_FLAG_PROFILE,
+ * MUON_FLAG_STAGED_ONLY and MUON_FLAG_ONE_STREAM. *out receives the context; it is owned by the
  * caller until muon_destroy. No device memory is allocated (the device's copy of the
  * muon_step_static scratch array comes with the library's code, which this call looks up). */
 int muon_init(muon_ctx **out, int device, uint32_t flags);
@@ -192,12 +193,13 @@ int muon_workspace_size(muon_ctx *ctx, const muon_matrix *mats, int count,
  * step that meets a new (stage, shape, batch) times the candidate tile configurations on
  * its own workspace buffers, synchronising the stream once for it, and caches the
  * fastest for the process; later steps make no host synchronisation.
- * Concurrency: once every shape group of the list has its tiles measured, independent
- * groups (matrices of one canonical shape) run on up to four streams: `stream` and
- * streams the context creates on its device at default priority, forked from `stream`
- * and joined back into it with events, so the work still completes in `stream`'s order
- * for the caller (also under stream capture). With MUON_FLAG_PROFILE all launches stay
- * on `stream`. */
+ * Concurrency: once every shape group of the list has its tiles measured, groups
+ * (matrices of one canonical shape) too small to fill the GPU (under 1e11 FLOPs of update)
+ * run on up to three streams beside `stream`, which runs the larger groups in order; the
+ * extra streams are created by the context on its device at default priority, forked from
+ * `stream` and joined back into it with events, so the work still completes in `stream`'s
+ * order for the caller (also under stream capture). With MUON_FLAG_PROFILE or
+ * MUON_FLAG_ONE_STREAM all launches stay on `stream`. */
 int muon_step(muon_ctx *ctx, const muon_matrix *mats, int count, const muon_hparams *hp,
               void *workspace, size_t workspace_bytes, void *stream);
 
@@ -269,8 +271,8 @@ int muon_plan_info(muon_ctx *ctx, const muon_matrix *mats, int count,
  * 0 = 64x64, 1 = 128x128, 2 = 256x128 (kind 2 only), 3 = 256x256; with direct global->LDS
  * loads: 4 = 64x64, 5 = 128x128, 6 = 256x128 (kind 2 only), 7 = 256x256, 8 = 256x256 with
  * 4 waves, 9 = 64x64 and 10 = 128x128 with two k-groups, 11 = 256x256 with 64-byte K
- * slices, 12 = 128x128 with two k-groups and 64-byte K slices, 13 = 256x192 (kind 2 only);
- * 2, 3, 6, 7, 8, 11 and 13 not fp32);
+ * slices, 12 = 128x128 with two k-groups and 64-byte K slices, 13 = 256x192 (kind 2 only),
+ * 14 = 256x256 with 4 waves and 64-byte K slices; 2, 3, 6, 7, 8, 11, 13 and 14 not fp32);
  * an unavailable combination returns MUON_ERR_UNSUPPORTED.
  * Leading dimensions equal the column counts; M, N, K must be multiples of 64. */
 int muon_debug_gemm(muon_ctx *ctx, int kind, int ns_dtype, int tile, int64_t M, int64_t N,

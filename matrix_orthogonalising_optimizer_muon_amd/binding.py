@@ -43,6 +43,7 @@ MUON_MAX_SEGMENTS = 8
 MUON_FLAG_MODEL_ONLY = 1
 MUON_FLAG_PROFILE = 2
 MUON_FLAG_STAGED_ONLY = 4
+MUON_FLAG_ONE_STREAM = 8
 
 DTYPES = {"f32": MUON_F32, "bf16": MUON_BF16}
 MODES = {"auto": MUON_NS_AUTO, "plain": MUON_NS_PLAIN, "gram": MUON_NS_GRAM,

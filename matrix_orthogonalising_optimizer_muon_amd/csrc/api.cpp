@@ -592,6 +592,11 @@ bool group_tuned(const muon_ctx* ctx, const Group& g, const muon_hparams& hp, bo
 
 constexpr int kMaxLanes = 4;  // streams per step, the caller's included
 
+// A group whose update is at least 1e11 FLOPs (about 0.1 ms of MFMA work) keeps the whole GPU
+// busy with its own launches; running another such group beside it only makes them compete
+// for the CUs and the caches.
+bool fills_gpu(const Group& g) { return g.work >= 1e11; }
+
 // Creates the context's extra streams and events (default priority) up to `n` lanes.
 bool ensure_lanes(muon_ctx* ctx, int n) {
   if (!ctx->lane_fork && hipEventCreateWithFlags(&ctx->lane_fork, hipEventDisableTiming) != hipSuccess) {
@@ -835,11 +840,17 @@ int step_impl(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
         tm.done();
       }
     }
-    // Independent shape groups run on up to kMaxLanes streams (largest work first, each
-    // to the least loaded lane) when none of them still has tiles to measure and the
-    // context does not profile; otherwise all run on the caller's stream in order.
-    int nl = std::min<int>(kMaxLanes, static_cast<int>(plan.groups.size()));
-    if ((ctx->flags & MUON_FLAG_PROFILE) || no_alloc) nl = 1;
+    // Independent shape groups whose launches do not fill the GPU run on up to
+    // kMaxLanes - 1 extra streams beside the caller's (largest work first, each to the least
+    // loaded lane), when none of them still has tiles to measure and the context does not
+    // profile; groups that fill the GPU run in order on the caller's stream. (Measured on the
+    // 7B list, whose three groups all fill the GPU: 314 ms on one stream, 324 ms with the
+    // groups on four streams; on the 832-matrix list, none of whose groups does: 0.69 ms on
+    // four streams, 0.75 ms on one.)
+    int small = 0;
+    for (const Group& g : plan.groups) small += fills_gpu(g) ? 0 : 1;
+    int nl = std::min<int>(kMaxLanes, small + (small < static_cast<int>(plan.groups.size()) ? 1 : 0));
+    if ((ctx->flags & (MUON_FLAG_PROFILE | MUON_FLAG_ONE_STREAM)) || no_alloc || small == 0) nl = 1;
     for (size_t i = 0; nl > 1 && i < plan.groups.size(); ++i)
       if (!group_tuned(ctx, plan.groups[i], *hp, env.f32)) nl = 1;
     if (nl > 1 && !ensure_lanes(ctx, nl)) nl = 1;
@@ -855,7 +866,8 @@ int step_impl(muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hpar
     std::vector<double> load(nl, 0.0);
     int r = MUON_OK;
     for (const Group& g : plan.groups) {
-      const int l = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+      // groups that fill the GPU stay on the caller's stream (lane 0)
+      const int l = fills_gpu(g) ? 0 : static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
       load[l] += g.work;
       StepEnv le = env;
       if (l > 0) le.st = ctx->lanes[l - 1];
@@ -907,7 +919,8 @@ int muon_init(muon_ctx** out, int device, uint32_t flags) {
   try {
     if (!out) return MUON_ERR_ARG;
     *out = nullptr;
-    if ((flags & ~(MUON_FLAG_MODEL_ONLY | MUON_FLAG_PROFILE | MUON_FLAG_STAGED_ONLY)) != 0) return MUON_ERR_ARG;
+    if ((flags & ~(MUON_FLAG_MODEL_ONLY | MUON_FLAG_PROFILE | MUON_FLAG_STAGED_ONLY | MUON_FLAG_ONE_STREAM)) != 0)
+      return MUON_ERR_ARG;
     if (device == -1) {  // host-only context: planning and validation, no launches
       muon_ctx* c = new (std::nothrow) muon_ctx;
       if (!c) return MUON_ERR_HIP;

@@ -182,17 +182,20 @@ __device__ __forceinline__ void w_store4(const GemmParams& p, const MatDesc& d, 
   }
 }
 
-// Tile index of this workgroup: XCD-aware remap, then grouped (8-tile-row) ordering for
+// Matrix and tile of this workgroup: XCD-aware remap, then grouped (8-tile-row) ordering for
 // general outputs or an upper-triangle walk for symmetric ones.
 template <bool SYM>
-__device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& tn) {
-  // Workgroups are dealt round-robin to the 8 XCDs (workgroup i runs on XCD i % 8); give
-  // each XCD a contiguous run of logical tiles so neighbouring tiles (shared operand
-  // panels) share one L2. XCD x holds nwg/8 tiles, plus one if x < nwg % 8.
-  const int i = blockIdx.x;
-  const int nwg = gridDim.x;
+__device__ __forceinline__ void tile_coords(const GemmParams& p, int& mat, int& tm, int& tn) {
+  // Workgroups are dealt round-robin to the 8 XCDs in the order of their linear id
+  // (x fastest, then y = matrix): workgroup i runs on XCD i % 8. Give each XCD a contiguous
+  // run of the launch's logical (matrix, tile) sequence, so neighbouring tiles (shared
+  // operand panels) share one L2. XCD x holds nwg/8 of them, plus one if x < nwg % 8.
+  const int i = blockIdx.x + blockIdx.y * gridDim.x;
+  const int nwg = gridDim.x * gridDim.y;
   const int x = i & 7, q = nwg >> 3, r = nwg & 7;
-  int t = x * q + min(x, r) + (i >> 3);
+  const int tt = x * q + min(x, r) + (i >> 3);
+  mat = tt / p.tiles;
+  int t = tt - mat * p.tiles;
   if constexpr (SYM) {
     int row = 0;
     int len = p.tiles_n;
@@ -205,9 +208,9 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
     const int g = t / group;
     const int first = g * GM;
     const int gm = min(p.tiles_m - first, GM);
-    const int r = t - g * group;
-    tm = first + r % gm;
-    tn = r / gm;
+    const int r2 = t - g * group;
+    tm = first + r2 % gm;
+    tn = r2 / gm;
   }
 }
 
@@ -467,10 +470,8 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   const int wave = tid >> 6;
   const int kgrp = wave / NWC;     // which k-steps of every slice this wave computes
   const int wloc = wave % NWC;     // which wave tile of the output
-  const int mat = blockIdx.y;
-
-  int tm, tn;
-  tile_coords<SYM>(p, tm, tn);
+  int mat, tm, tn;
+  tile_coords<SYM>(p, mat, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const char* Ab = static_cast<const char*>(p.A) + static_cast<int64_t>(mat) * p.sA * ES;
@@ -726,10 +727,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmParams p) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int mat = blockIdx.y;
-
-  int tm, tn;
-  tile_coords<SYM>(p, tm, tn);
+  int mat, tm, tn;
+  tile_coords<SYM>(p, mat, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const char* Ab = static_cast<const char*>(p.A) + static_cast<int64_t>(mat) * p.sA * ES;
@@ -906,6 +905,9 @@ hipError_t launch_tile(int cfg, const GemmParams& p, hipStream_t st) {
       if constexpr (KIND != KIND_F32) return launch_dma<KIND, 256, 256, 2, 4, 4, SYM, EPI, TAG, 1, 4>(p, st);
       return hipErrorInvalidValue;
     case TILE_128_DMA_K2_H: return launch_dma<KIND, 128, 128, 2, 2, 8, SYM, EPI, TAG, 2, 4>(p, st);
+    case TILE_256_DMA4_H:  // 4 waves of 128 x 128, 64-byte slices: 4 stages, three slices in flight
+      if constexpr (KIND != KIND_F32) return launch_dma<KIND, 256, 256, 2, 2, 4, SYM, EPI, TAG, 1, 4>(p, st);
+      return hipErrorInvalidValue;
     case TILE_256x192_DMA:  // 8 waves, wave tile 64 x 96: 2560 x 9728 is 510 tiles, two full rounds of 256 CUs
       if constexpr (!SYM && KIND != KIND_F32) return launch_dma<KIND, 256, 192, 4, 2, 2, SYM, EPI, TAG>(p, st);
       return hipErrorInvalidValue;

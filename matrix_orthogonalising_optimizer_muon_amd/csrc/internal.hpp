@@ -76,14 +76,15 @@ enum TileCfg : int {
   TILE_256_DMA_H = 11,   // as TILE_256_DMA with 64-byte slices: 4 LDS stages
   TILE_128_DMA_K2_H = 12,  // as TILE_128_DMA_K2 with 64-byte slices: 8 LDS stages
   TILE_256x192_DMA = 13,  // 256 x 192, 8 waves, wave tile 64 x 96, 2 LDS stages
-  TILE_COUNT = 14
+  TILE_256_DMA4_H = 14,   // as TILE_256_DMA4 with 64-byte slices: 4 LDS stages
+  TILE_COUNT = 15
 };
 inline int tile_bm(int cfg) {
-  static const int bm[TILE_COUNT] = {64, 128, 256, 256, 64, 128, 256, 256, 256, 64, 128, 256, 128, 256};
+  static const int bm[TILE_COUNT] = {64, 128, 256, 256, 64, 128, 256, 256, 256, 64, 128, 256, 128, 256, 256};
   return bm[cfg];
 }
 inline int tile_bn(int cfg) {
-  static const int bn[TILE_COUNT] = {64, 128, 128, 256, 64, 128, 128, 256, 256, 64, 128, 256, 128, 192};
+  static const int bn[TILE_COUNT] = {64, 128, 128, 256, 64, 128, 128, 256, 256, 64, 128, 256, 128, 192, 256};
   return bn[cfg];
 }
 

@@ -118,7 +118,7 @@ def test_profile_read_errors(hctx):
 def test_init_errors():
     out = ctypes.c_void_p()
     assert B._lib.muon_init(None, 0, 0) == B.MUON_ERR_ARG
-    assert B._lib.muon_init(ctypes.byref(out), -1, 8) == B.MUON_ERR_ARG
+    assert B._lib.muon_init(ctypes.byref(out), -1, 16) == B.MUON_ERR_ARG
     assert B._lib.muon_init(ctypes.byref(out), 9999, 0) == B.MUON_ERR_DEVICE
     assert B._lib.muon_destroy(None) == B.MUON_OK
 
@@ -165,12 +165,15 @@ def test_workspace_errors(hctx):
     assert step(hctx, shapes, wsb=need) == B.MUON_ERR_DEVICE
 
 
+B_TILE_COUNT = 15   # tile ids muon_debug_gemm documents: 0..14
+
+
 def test_debug_gemm_validation(hctx):
     f = B._lib.muon_debug_gemm
     P = ctypes.c_void_p(FAKE)
     # f(ctx, kind, ns_dtype, tile_cfg, M, N, K, A, B, E, C, C2, alpha, beta, gamma, oscale, stream)
     assert f(hctx, 3, 1, 0, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
-    assert f(hctx, 0, 1, 14, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
+    assert f(hctx, 0, 1, B_TILE_COUNT, 64, 64, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
     assert f(hctx, 0, 1, 6, 256, 256, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
     assert f(hctx, 0, 1, 0, 64, 64, 100, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
     assert f(hctx, 1, 1, 0, 64, 128, 64, P, P, None, P, None, 1.0, 0.0, 0.0, 1.0, None) == B.MUON_ERR_ARG
@@ -283,7 +286,7 @@ def test_tune_cache_round_trip(hctx, tmp_path):
     "2 1 2560 9728 1 7\n",          # 256 tile on the fp32 path
     "2 0 2500 9728 1 1\n",          # not a multiple of 64
     "2 0 2560 9728 0 1\n",          # empty batch
-    "2 0 2560 9728 1 14\n",         # unknown tile
+    "2 0 2560 9728 1 15\n",         # unknown tile
     "2 0 2560 9728 1 x\n",
 ])
 def test_tune_cache_rejects_bad_files(hctx, tmp_path, text):

@@ -97,7 +97,7 @@ __device__ __forceinline__ void zero(f32x16& a) {
   for (int e = 0; e < 16; ++e) a[e] = 0.0f;
 }
 
-template <int MP, int NT>
+template <int MP, int NT, int NPMAX>
 __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
   constexpr int NW = NT / 64;                 // waves
   constexpr int CS = MP / 8;                  // chunks per row of an m' x m' matrix
@@ -120,8 +120,10 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
   constexpr int AP_ASTRIDE = 32 * NW / 2;
 
   // LDS: the four m' x m' matrices and the staging slice; before the recurrence starts
-  // the same space holds U (at most kSmallMaxElems bf16 values).
-  constexpr int SMQ = (4 * SQ + STG) > kSmallMaxElems / 8 ? (4 * SQ + STG) : kSmallMaxElems / 8;
+  // the same space holds xs * X0 (MP x NPMAX fp16 values at most). Sizing it by the group's
+  // n' lets several workgroups of a short-row group share a CU.
+  static_assert(MP * NPMAX <= kSmallMaxElems, "single-workgroup size bound");
+  constexpr int SMQ = (4 * SQ + STG) > MP * NPMAX / 8 ? (4 * SQ + STG) : MP * NPMAX / 8;
   static_assert(SMQ % STG == 0 && SQ % STG == 0, "stage slots");
   constexpr int NR0 = SMQ / STG - SQ / STG;   // staging slices besides one m' x m' matrix
   constexpr int NR = NR0 > 8 ? 8 : NR0;
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
   //    deterministic), the second stores M' and writes X0 = xs * s * U, rounded once to
   //    fp16, to LDS in the canonical layout (the recurrence's LDS is free until step 3).
   u16* U = reinterpret_cast<u16*>(sm);   // MP x Np fp16, row-major: xs * X0
-  static_assert(sizeof(sm) >= static_cast<size_t>(kSmallMaxElems) * 2, "X0 fits in LDS");
+  static_assert(sizeof(sm) >= static_cast<size_t>(MP) * NPMAX * 2, "X0 fits in LDS");
   {
     const int total = MP * Np;
     for (int i = tid * 8; i < total; i += NT * 8) *reinterpret_cast<uint4*>(U + i) = make_uint4(0, 0, 0, 0);
@@ -211,12 +213,22 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
     load_gm(gi, g, m);
     momentum8(g, m, mn, u);
   };
+  // Each pass takes UB groups of 8 per thread and iteration, every load of the batch issued
+  // before any arithmetic (indices past the end are clamped and their values dropped), so a
+  // thread has UB * 2 loads in flight instead of one round trip per group.
+  constexpr int UB = 4;
+  const int ngr = rows * gpr;
   float sq = 0.0f;
-  for (int gi = tid; gi < rows * gpr; gi += NT) {
-    float mn[8], u[8];
-    momentum_u(gi, mn, u);
+  for (int g0 = tid; g0 < ngr; g0 += NT * UB) {
+    float mn[UB][8], u[UB][8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) sq += u[k] * u[k];   // zero past the row end
+    for (int b = 0; b < UB; ++b) momentum_u(min(g0 + b * NT, ngr - 1), mn[b], u[b]);
+#pragma unroll
+    for (int b = 0; b < UB; ++b)
+      if (g0 + b * NT < ngr) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sq += u[b][k] * u[b][k];   // zero past the row end
+      }
   }
   red[tid] = static_cast<double>(sq);
   __syncthreads();
@@ -226,17 +238,23 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
   }
   const float s = static_cast<float>(1.0 / (sqrt(red[0]) + static_cast<double>(p.eps)));
   const float xsc = p.xs * s;
-  for (int gi = tid; gi < rows * gpr; gi += NT) {
-    float mn[8], u[8];
-    momentum_u(gi, mn, u);
-    const int sr = gi / gpr, sc0 = (gi % gpr) * 8;
-    const int64_t base = static_cast<int64_t>(sr) * cols + sc0;
+  for (int g0 = tid; g0 < ngr; g0 += NT * UB) {
+    float mn[UB][8], u[UB][8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (sc0 + k >= cols) continue;
-      if (!p.dry) store_elem(d.M, base + k, mn[k], p.m_bf16);
-      const int r = d.transposed ? sc0 + k : sr, c = d.transposed ? sr : sc0 + k;
-      U[r * Np + c] = f32_to_f16(xsc * u[k]);
+    for (int b = 0; b < UB; ++b) momentum_u(min(g0 + b * NT, ngr - 1), mn[b], u[b]);
+#pragma unroll
+    for (int b = 0; b < UB; ++b) {
+      const int gi = g0 + b * NT;
+      if (gi >= ngr) continue;
+      const int sr = gi / gpr, sc0 = (gi % gpr) * 8;
+      const int64_t base = static_cast<int64_t>(sr) * cols + sc0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (sc0 + k >= cols) continue;
+        if (!p.dry) store_elem(d.M, base + k, mn[b][k], p.m_bf16);
+        const int r = d.transposed ? sc0 + k : sr, c = d.transposed ? sr : sc0 + k;
+        U[r * Np + c] = f32_to_f16(xsc * u[b][k]);
+      }
     }
   }
   __syncthreads();
@@ -471,10 +489,14 @@ __global__ __launch_bounds__(NT) void small_ns_kernel(const SmallParams p) {
 
 hipError_t launch_small_ns(const SmallParams& p, hipStream_t st) {
   if (p.count <= 0) return hipSuccess;
-  if (p.Mp == 64) {
-    hipLaunchKernelGGL((small_ns_kernel<64, 256>), dim3(p.count), dim3(256), 0, st, p);
+  // m' = 64: LDS sized for n' <= 256 (three workgroups per CU) or for the largest n';
+  // m' = 128: eight waves (two per SIMD), one workgroup per CU.
+  if (p.Mp == 64 && p.Np <= 256) {
+    hipLaunchKernelGGL((small_ns_kernel<64, 256, 256>), dim3(p.count), dim3(256), 0, st, p);
+  } else if (p.Mp == 64) {
+    hipLaunchKernelGGL((small_ns_kernel<64, 256, kSmallMaxElems / 64>), dim3(p.count), dim3(256), 0, st, p);
   } else if (p.Mp == 128) {
-    hipLaunchKernelGGL((small_ns_kernel<128, 256>), dim3(p.count), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((small_ns_kernel<128, 512, kSmallMaxElems / 128>), dim3(p.count), dim3(512), 0, st, p);
   } else {
     return hipErrorInvalidValue;
   }

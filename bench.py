@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--mode", default="auto", choices=["auto", "gram", "plain", "auto_schedule"],
                     help="NS form: auto (plain or Gram 2+2+1 per shape, the default), gram, plain, or "
                          "auto_schedule (plain or Gram with the cheapest segment count per shape)")
+    ap.add_argument("--also-modes", default="auto_schedule",
+                    help="comma-separated further NS forms timed on the primary workload in the same run "
+                         "(reported under \"modes\": ms per step, plan, GEMM rate); empty for none")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one muon_step captured in a HIP graph (after the warm-up "
                          "has measured the tiles) instead of eager calls")
@@ -214,14 +217,14 @@ NS_DESC = {"auto": "auto: plain NS (5 rounds) or Gram NS 2+2+1 per shape, by mea
                             "per shape by measured stage cost"}
 
 
-def run_workload(w, args, B, torch, ctx, pctx, primary):
+def run_workload(w, args, B, torch, ctx, pctx, primary, mode=None):
     """Inputs resident in HBM, warm-up (measures the tiles), K event-timed steps, then K
     steps with per-launch events for the stage table. Frees its buffers on return."""
     print(f"[bench] workload {w.name}: {len(w.matrices)} matrices, {w.elements / 1e6:.1f} M elements",
           file=sys.stderr, flush=True)
     Ws, Gs, Ms, data = make_inputs(w, torch)
     mats = list(zip(Ws, Gs, Ms))
-    hp = B.make_hparams(lr=w.lr, momentum=w.mu, weight_decay=w.wd, mode=args.mode,
+    hp = B.make_hparams(lr=w.lr, momentum=w.mu, weight_decay=w.wd, mode=mode or args.mode,
                         w_dtype=w.w_dtype, g_dtype=w.g_dtype, m_dtype=w.m_dtype, ns_dtype=w.ns_dtype)
     arr = B.matrix_list(mats, hp, 0)
     nbytes = B.muon_workspace_size(ctx, mats, hp)
@@ -435,6 +438,19 @@ def main():
                                  **{k: sa[k] for k in ("roofline", "gemm_tflops", "gemm_frac_of_peak",
                                                        "momentum_gbs", "hbm_phase_gbs", "profiled_ms_per_step",
                                                        "stages")}}
+    modes = [x for x in args.also_modes.split(",") if x and x != args.mode] if args.also_modes else []
+    if modes:
+        # the same workload with another Newton-Schulz form (same 5 rounds); the headline value
+        # stays the form selected by --mode
+        out["modes"] = {}
+        for mname in modes:
+            rm = run_workload(w, args, B, torch, ctx, pctx, primary=False, mode=mname)
+            smm = summarise(w, rm, args)
+            smm.pop("dom")
+            out["modes"][mname] = {"ns": NS_DESC[mname], "ms_per_step": round(rm["ms"], 4),
+                                   "step_ms_p10_p50_p90": [round(x, 4) for x in rm["pct"]],
+                                   "plan": rm["plans"],
+                                   **{k: smm[k] for k in ("gemm_tflops", "gemm_frac_of_peak", "profiled_ms_per_step")}}
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)

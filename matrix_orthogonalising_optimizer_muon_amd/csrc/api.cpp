@@ -238,6 +238,10 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
       g.hs.mode = g.mode;
       g.tile_sq = heuristic_sym(g.Mp, cnt, ctx->cu_count);
       g.tile_ap = heuristic_apply(g.Mp, g.Np, cnt, ctx->cu_count, f32);
+      if (!dma_addressable(g.Mp, g.Np, g.Mp, g.Np, static_cast<int64_t>(ex))) {
+        g.tile_sq = staged_tile(g.tile_sq);
+        g.tile_ap = staged_tile(g.tile_ap);
+      }
       g.work = kernel_flops(m, n, g.mode, g.hs) * cnt;
       plan.groups.push_back(std::move(g));
     }
@@ -427,6 +431,9 @@ template <class Build>
 hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristic, bool sym,
                      Build build, int* used) {
   muon_ctx* ctx = env.ctx;
+  // every operand of the group's stages is at most Mp x Np elements
+  const bool dma_ok = dma_addressable(g.Mp, g.Np, g.Mp, g.Np, env.f32 ? 4 : 2);
+  auto usable = [&](int c) { return dma_ok ? c : staged_tile(c); };
   int cfg = heuristic;
   if (!(ctx->flags & MUON_FLAG_MODEL_ONLY)) {
     const int key_op = (op == OP_UPDATE) ? OP_APPLY : op;
@@ -459,6 +466,7 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
         if (g.Mp >= 256) cands = {TILE_256_DMA, TILE_256x192_DMA, TILE_256x128_DMA};
         for (int c : {TILE_128_DMA_K2, TILE_128, TILE_64}) cands.push_back(c);
       }
+      for (int& c : cands) c = usable(c);
       for (int i = 0; i < 2; ++i)
         if (!ctx->tune_ev[i] && hipEventCreate(&ctx->tune_ev[i]) != hipSuccess) return hipErrorUnknown;
       const GemmOp top = (op == OP_UPDATE) ? OP_APPLY : op;
@@ -490,6 +498,7 @@ hipError_t run_stage(const StepEnv& env, const Group& g, GemmOp op, int heuristi
       g_tuned_ms[key] = chosen;
     }
   }
+  cfg = usable(cfg);
   const GemmParams p = build(cfg);
   *used = cfg;
   return launch_gemm(op, env.f32, cfg, p, env.st);
@@ -1149,6 +1158,10 @@ int muon_plan_info(muon_ctx* ctx, const muon_matrix* mats, int count, const muon
       auto b = g_tuned.find(std::make_tuple(ctx->device, static_cast<int>(OP_APPLY), f32, g.Mp, g.Np, cnt));
       if (b != g_tuned.end()) out->tile_apply = b->second;
     }
+    if (!g.single_wg && !dma_addressable(g.Mp, g.Np, g.Mp, g.Np, hp->ns_dtype == MUON_F32 ? 4 : 2)) {
+      out->tile_sym = staged_tile(out->tile_sym);
+      out->tile_apply = staged_tile(out->tile_apply);
+    }
     out->dense_flops = dense_flops(g.m, g.n, g.mode, g.hs);
     out->kernel_flops = g.single_wg ? out->dense_flops : kernel_flops(g.m, g.n, g.mode, g.hs);
     std::memset(out->segments, 0, sizeof(out->segments));
@@ -1251,6 +1264,7 @@ int muon_debug_gemm(muon_ctx* ctx, int kind, int ns_dtype, int tile, int64_t M, 
         K > kMaxDim)
       return MUON_ERR_ARG;
     if ((kind == 0 || kind == 1) && (M != N || tile_bm(tile) != tile_bn(tile))) return MUON_ERR_ARG;
+    if (!dma_addressable(M, K, N, K, ns_dtype == MUON_F32 ? 4 : 2)) tile = staged_tile(tile);
     if (ctx->device < 0) return MUON_ERR_DEVICE;
     DeviceGuard dg(ctx->device);
     if (!dg.ok) return MUON_ERR_HIP;

@@ -422,6 +422,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 // The same, and every LDS access of this wave returned (lgkmcnt 0).
+// Buffer resource over `bytes` bytes from `base` (raw buffer: no stride, no format
+// conversion; accesses at or past `bytes` return zero instead of faulting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+// 16 bytes per lane from the buffer at voff + soff into LDS: lane l writes bytes
+// [16 l, 16 l + 16) of the instruction's window at lds_dst (the M0 base).
+__device__ __forceinline__ void buf_load_lds(__amdgpu_buffer_rsrc_t r, void* lds_dst, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt");
@@ -467,7 +478,9 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Wave-uniform (scalar): every LDS window address derived from it stays in SGPRs, so a
+  // load's M0 is set by scalar arithmetic.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kgrp = wave / NWC;     // which k-steps of every slice this wave computes
   const int wloc = wave % NWC;     // which wave tile of the output
   int mat, tm, tn;
@@ -477,36 +490,36 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_dma_kernel(const GemmP
   const char* Ab = static_cast<const char*>(p.A) + static_cast<int64_t>(mat) * p.sA * ES;
   const char* Bb = static_cast<const char*>(p.B) + static_cast<int64_t>(mat) * p.sB * ES;
 
-  int64_t a_off[IA], b_off[IB];
+  // Operands are read as buffers over this matrix's A and B: a lane's byte offset within
+  // the matrix (32 bits; the host runs these kernels only where every operand is under
+  // 4 GiB) plus the slice's K offset as the scalar offset, so a load needs no per-lane
+  // address arithmetic.
+  uint32_t a_off[IA], b_off[IB];
 #pragma unroll
   for (int j = 0; j < IA; ++j) {
     const int row = (wave * IA + j) * RPI + lane / CH;
     const int chunk = (lane % CH) ^ swz_bits<CH>(row);
     const int gr = min(m0 + row, p.M - 1);
-    a_off[j] = (static_cast<int64_t>(gr) * p.lda + chunk * VEC) * ES;
+    a_off[j] = static_cast<uint32_t>((static_cast<int64_t>(gr) * p.lda + chunk * VEC) * ES);
   }
 #pragma unroll
   for (int j = 0; j < IB; ++j) {
     const int row = (wave * IB + j) * RPI + lane / CH;
     const int chunk = (lane % CH) ^ swz_bits<CH>(row);
     const int gr = min(n0 + row, p.N - 1);
-    b_off[j] = (static_cast<int64_t>(gr) * p.ldb + chunk * VEC) * ES;
+    b_off[j] = static_cast<uint32_t>((static_cast<int64_t>(gr) * p.ldb + chunk * VEC) * ES);
   }
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, static_cast<uint32_t>(static_cast<int64_t>(p.M) * p.lda * ES));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, static_cast<uint32_t>(static_cast<int64_t>(p.N) * p.ldb * ES));
 
-  typedef __attribute__((address_space(3))) void* lds_ptr;
-  typedef const __attribute__((address_space(1))) void* glb_ptr;
   auto issue = [&](int stage, int k0) {
-    const int64_t kb = static_cast<int64_t>(k0) * ES;
+    const int kb = k0 * ES;
     u32x4* sa = lds + stage * STAGE;
     u32x4* sb = sa + BM * CH;
 #pragma unroll
-    for (int j = 0; j < IA; ++j)
-      __builtin_amdgcn_global_load_lds((glb_ptr)(Ab + a_off[j] + kb),
-                                       (lds_ptr)(sa + (wave * IA + j) * RPI * CH), 16, 0, 0);
+    for (int j = 0; j < IA; ++j) buf_load_lds(ra, sa + (wave * IA + j) * RPI * CH, a_off[j], kb);
 #pragma unroll
-    for (int j = 0; j < IB; ++j)
-      __builtin_amdgcn_global_load_lds((glb_ptr)(Bb + b_off[j] + kb),
-                                       (lds_ptr)(sb + (wave * IB + j) * RPI * CH), 16, 0, 0);
+    for (int j = 0; j < IB; ++j) buf_load_lds(rb, sb + (wave * IB + j) * RPI * CH, b_off[j], kb);
   };
 
   f32x16 acc[FM][FN];

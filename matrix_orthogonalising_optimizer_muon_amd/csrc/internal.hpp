@@ -97,6 +97,23 @@ inline bool tile_available(bool sym, bool f32, int cfg) {
   return true;
 }
 
+// The direct-load kernels address a matrix's operands with 32-bit byte offsets. A stage
+// whose operands (A: M x lda, B: N x ldb elements of `es` bytes) do not fit runs the
+// register-staged tile of the same block rows instead.
+inline bool dma_addressable(int64_t M, int64_t lda, int64_t N, int64_t ldb, int64_t es) {
+  const int64_t lim = (int64_t{1} << 32) - 1;
+  return M * lda * es <= lim && N * ldb * es <= lim;
+}
+inline int staged_tile(int cfg) {
+  switch (cfg) {
+    case TILE_64_DMA: case TILE_64_DMA_K2: return TILE_64;
+    case TILE_128_DMA: case TILE_128_DMA_K2: case TILE_128_DMA_K2_H: return TILE_128;
+    case TILE_256_DMA: case TILE_256_DMA4: case TILE_256_DMA_H: case TILE_256_DMA4_H: return TILE_256;
+    case TILE_256x128_DMA: case TILE_256x192_DMA: return TILE_256x128;
+    default: return cfg;
+  }
+}
+
 // Launch one batched GEMM stage. ns_f32: fp32 kernels, else bf16/fp16 kernels.
 hipError_t launch_gemm(GemmOp op, bool ns_f32, int cfg, const GemmParams& p, hipStream_t st);
 

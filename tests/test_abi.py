@@ -461,3 +461,14 @@ def test_debug_stage_validation_on_host(hctx):
     bad = B.make_hparams(momentum=2.0)
     assert B._lib.muon_debug_stage(hctx, 0, ctypes.byref(m), ctypes.byref(bad), None, ctypes.c_void_p(64),
                                    None, ctypes.byref(f), ctypes.c_void_p(256), 4096, None) == B.MUON_ERR_ARG
+
+
+def test_plan_huge_operands_use_staged_tiles(hctx):
+    """The direct-load kernels address a matrix's operands with 32-bit offsets: a shape whose
+    padded iterate exceeds 4 GiB (32768 x 65600 fp16) is planned on register-staged tiles
+    (ids 0-3); 32768 x 65472 (just under 2^32 bytes) keeps the direct-load ones."""
+    staged = {0, 1, 2, 3}
+    big, = plan(hctx, [(32768, 65600)], mode="gram")
+    assert big.tile_sym in staged and big.tile_apply in staged
+    ok, = plan(hctx, [(32768, 65472)], mode="gram")
+    assert ok.tile_apply not in staged

@@ -58,9 +58,10 @@ def check_elems(got, ref, K, u_out):
 
 # tile configurations: 0 = 64x64, 1 = 128x128, 2 = 256x128 (apply only), 3 = 256x256;
 # 4-7: the same tiles with direct global -> LDS loads; 8: 256x256 with 4 waves; 9, 10:
-# 64 and 128 tiles with two k-groups; 11, 12: 256 and 128 (two k-groups) with 64-byte slices
-SYM_TILES = [0, 1, 3, 4, 5, 7, 8, 9, 10, 11, 12]
-ALL_TILES = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13]
+# 64 and 128 tiles with two k-groups; 11, 12: 256 and 128 (two k-groups) with 64-byte slices;
+# 13: 256x192 (apply only); 14: 256x256 with 4 waves and 64-byte slices
+SYM_TILES = [0, 1, 3, 4, 5, 7, 8, 9, 10, 11, 12, 14]
+ALL_TILES = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14]
 F32_TILES = [0, 1, 4, 5, 9, 10, 12]
 
 

@@ -64,7 +64,9 @@ typedef struct muon_ctx muon_ctx; /* opaque; owned by the library */
 
 /* One 2-D weight. All three arrays are rows x cols, row-major, leading dimension cols,
  * on the context's device, in the dtypes named by muon_hparams. W and M are updated in
- * place; G is read only. Arrays of different matrices must not overlap. */
+ * place; G is read only. Arrays of different matrices must not overlap. rows and cols
+ * are each in [1, 2^20] (else MUON_ERR_ARG). A shape whose padded iterate exceeds 4 GiB
+ * (past the direct-load tiles' 32-bit offsets) runs on the register-staged tiles. */
 typedef struct muon_matrix {
   void *W;
   const void *G;

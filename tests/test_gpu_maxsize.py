@@ -1,0 +1,189 @@
+"""Parity at the largest shapes the library accepts: one dimension at 2^20 (the
+per-dimension limit of muon_step), in one call over three matrices: 2048 x 2^20 stored wide
+and 2^20 x 2048 stored tall (one shape group of two: 2^31 elements each, so element counts,
+offsets and the batch stride pass 2^31), and 2^20 x 2040 stored tall (ragged m'). The
+padded fp16 iterate of each is 2048 x 2^20 x 2 bytes = 4 GiB, past the 32-bit offsets of
+the direct-load GEMM tiles, so these groups run on the register-staged tiles.
+
+No oracle can run Newton-Schulz on a 2048 x 2^20 matrix, so the input has a structure
+that makes the exact result computable block by block: in canonical (wide) coordinates
+G and M are zero except on 32 dense blocks, block t on a random set of about 64 rows and
+its own random set of 32768 columns (the row sets and the column sets each partition
+their axis). Then X X^T, every polynomial in it and Q X keep that block structure, and
+the Newton-Schulz result on block t is the oracle's on the block alone, started from the
+block divided by the Frobenius norm of the whole U (the sum of the blocks' squared
+norms: the rest is zero); `test_block_structure_premise` checks this against the
+oracle's whole step at a size it runs. Checked on the GPU:
+
+* everywhere off the blocks, W' equals W and M' is zero, bit for bit (every product
+  there sums exact zeros, so any value landing at a wrong address shows up);
+* on the blocks, O = (W - W') / lr within the bf16 path's relative Frobenius bar 2e-2
+  of the oracle's, and M' within bf16 rounding of the oracle's.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import muon as om
+
+COLS = 1 << 20                 # canonical n': the per-dimension limit
+SPECS = ((2048, False), (2048, True), (2040, True))   # canonical m', stored tall
+NBLK = 32
+LR, MU, EPS = 0.02, 0.95, 1e-7
+
+
+@pytest.fixture(scope="module")
+def B():
+    from matrix_orthogonalising_optimizer_muon_amd import binding
+    return binding
+
+
+def bf16_exact(a: np.ndarray) -> torch.Tensor:
+    """fp64 array -> CPU bf16 tensor (round to nearest even)."""
+    return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+
+
+def blocks(rng, nrows, ncols=COLS, nblk=NBLK):
+    rows = np.array_split(rng.permutation(nrows), nblk)
+    cols = np.array_split(rng.permutation(ncols), nblk)
+    return rows, cols
+
+
+def draw(rng, rows, cols):
+    """Blocks of G and M (bf16 values), block t scaled by 10 / (t + 1)."""
+    G, M = [], []
+    for t in range(len(rows)):
+        s = 10.0 / (t + 1)
+        shape = (len(rows[t]), len(cols[t]))
+        G.append(bf16_exact(s * rng.standard_normal(shape)))
+        M.append(bf16_exact(0.5 * s * rng.standard_normal(shape)))
+    return G, M
+
+
+def oracle_blocks(G, M):
+    """The oracle's M' and O on each block (global Frobenius norm over all blocks)."""
+    Mn, U = [], []
+    for g, m in zip(G, M):
+        mn, u = om.momentum(g.to(torch.float64).numpy(), m.to(torch.float64).numpy(), MU, True)
+        Mn.append(mn)
+        U.append(u)
+    norm = np.sqrt(sum(float(np.sum(u * u)) for u in U))
+    O = [om.newton_schulz_gram(u / (norm + EPS)) for u in U]
+    return Mn, O
+
+
+def place(dst, tall, r, c, vals):
+    """dst[canonical rows r, canonical cols c] = vals (canonical block), dst stored wide
+    (rows x cols) or tall (cols x rows)."""
+    ri = torch.as_tensor(r, device="cuda")
+    ci = torch.as_tensor(c, device="cuda")
+    if tall:
+        dst[ci[:, None], ri[None, :]] = vals.t().to(dst.dtype)
+    else:
+        dst[ri[:, None], ci[None, :]] = vals.to(dst.dtype)
+
+
+def take(src, tall, r, c):
+    ri = torch.as_tensor(r, device="cuda")
+    ci = torch.as_tensor(c, device="cuda")
+    return src[ci[:, None], ri[None, :]].t() if tall else src[ri[:, None], ci[None, :]]
+
+
+def test_block_structure_premise():
+    """On the CPU, at a size the oracle runs whole: the oracle's step on a block-structured
+    matrix (both orientations) is zero off the blocks and equals the per-block results with
+    the global norm on them, which is what the GPU test relies on."""
+    rng = np.random.default_rng(5)
+    nr, nc = 90, 1000
+    rows, cols = blocks(rng, nr, nc, 4)
+    Gb, Mb = draw(rng, rows, cols)
+    Mn, O = oracle_blocks(Gb, Mb)
+    for tall in (False, True):
+        G = np.zeros((nr, nc))
+        M = np.zeros((nr, nc))
+        W = rng.standard_normal((nr, nc))
+        for t in range(4):
+            G[np.ix_(rows[t], cols[t])] = Gb[t].double().numpy()
+            M[np.ix_(rows[t], cols[t])] = Mb[t].double().numpy()
+        if tall:
+            G, M, W = G.T.copy(), M.T.copy(), W.T.copy()
+        W_new, M_new, O_full = om.muon_step(W, G, M, lr=LR, mu=MU, wd=0.0, nesterov=True,
+                                            eps=EPS, mode="gram")
+        if tall:
+            O_full, M_new = O_full.T, M_new.T
+        mask = np.zeros((nr, nc), bool)
+        for t in range(4):
+            mask[np.ix_(rows[t], cols[t])] = True
+            assert np.allclose(O_full[np.ix_(rows[t], cols[t])], O[t], rtol=0, atol=1e-12)
+            assert np.array_equal(M_new[np.ix_(rows[t], cols[t])], Mn[t])
+        assert not O_full[~mask].any() and not M_new[~mask].any()
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(600)
+def test_max_dimension_block_structured(B):
+    rng = np.random.default_rng(20240920)
+    mats, ref, parts = [], [], []
+    for k, (nrows, tall) in enumerate(SPECS):
+        rows, cols = blocks(rng, nrows)
+        Gb, Mb = draw(rng, rows, cols)
+        ref.append(oracle_blocks(Gb, Mb))
+        parts.append((rows, cols))
+        shape = (COLS, nrows) if tall else (nrows, COLS)
+        G = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+        M = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+        for t in range(NBLK):
+            place(G, tall, rows[t], cols[t], Gb[t].cuda())
+            place(M, tall, rows[t], cols[t], Mb[t].cuda())
+        gen = torch.Generator(device="cuda").manual_seed(7 + k)
+        W = 0.02 * torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+        mats.append((W, G, M, tall))
+        print(f"[maxsize] matrix {k} ({'tall' if tall else 'wide'} {shape[0]}x{shape[1]}) placed",
+              flush=True)
+    W0 = [W.clone() for W, _, _, _ in mats]
+    torch.cuda.synchronize()
+
+    ctx = B.muon_init(0)
+    try:
+        hp = B.make_hparams(lr=LR, momentum=MU, weight_decay=0.0, eps=EPS, nesterov=True,
+                            mode="gram", segments=(2, 2, 1), w_dtype="f32", g_dtype="bf16",
+                            m_dtype="bf16", ns_dtype="bf16")
+        triples = [(W, G, M) for W, G, M, _ in mats]
+        for i in range(len(triples)):
+            entry = B.muon_plan_info(ctx, triples, hp, i)
+            assert entry.tile_sym in (0, 1, 2, 3) and entry.tile_apply in (0, 1, 2, 3), \
+                "a 4 GiB iterate must run on register-staged tiles"
+        nbytes = B.muon_workspace_size(ctx, triples, hp)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        print(f"[maxsize] muon_step over {len(triples)} matrices, workspace {nbytes / 2**30:.1f} GiB", flush=True)
+        B.check(B.muon_step(ctx, triples, hp, ws.data_ptr(), nbytes), "muon_step")
+        torch.cuda.synchronize()
+        print("[maxsize] step done", flush=True)
+        del ws
+    finally:
+        B.muon_destroy(ctx)
+
+    for k, (W, G, M, tall) in enumerate(mats):
+        Mn, O = ref[k]
+        rows, cols = parts[k]
+        D = W0[k] - W                      # lr * O on the blocks, exactly zero elsewhere
+        num = den = 0.0
+        worst_m = 0.0
+        for t in range(NBLK):
+            o_gpu = take(D, tall, rows[t], cols[t]).double().cpu().numpy() / LR
+            num += float(np.sum((o_gpu - O[t]) ** 2))
+            den += float(np.sum(O[t] ** 2))
+            m_gpu = take(M, tall, rows[t], cols[t]).double().cpu().numpy()
+            worst_m = max(worst_m, float(np.linalg.norm(m_gpu - Mn[t]) / np.linalg.norm(Mn[t])))
+            place(D, tall, rows[t], cols[t], torch.zeros(len(rows[t]), len(cols[t]), device="cuda"))
+            place(M, tall, rows[t], cols[t], torch.zeros(len(rows[t]), len(cols[t]), device="cuda"))
+        err = (num / den) ** 0.5
+        off_w = float(D.abs().max())
+        off_m = float(M.abs().max())
+        print(f"[maxsize] matrix {k}: O error {err:.3e}, M' error {worst_m:.3e}, "
+              f"off-block max |W' - W| {off_w}, max |M'| {off_m}", flush=True)
+        assert off_w == 0.0 and off_m == 0.0, (k, off_w, off_m)
+        assert err <= 2e-2, (k, err)
+        assert worst_m <= 2.0 ** -8, (k, worst_m)
+        del D

@@ -694,6 +694,13 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
   mp.count = count;
   mp.mu = hp.momentum; mp.nesterov = hp.nesterov;
   mp.g_bf16 = hp.g_dtype == MUON_BF16; mp.m_bf16 = hp.m_dtype == MUON_BF16; mp.x_f16 = !f32;
+  // The second pass reads G and M again. When a group's G and M fit well inside the 256 MB
+  // Infinity Cache, the first pass loads them normally so the second finds them there
+  // (2560 x 9728: second pass 50-51 -> 42 us, first pass +1 us); larger groups stream them
+  // past the caches (cached loads made their first pass 3% slower, the second no faster).
+  const double gm_bytes = static_cast<double>(count) * g.m * g.n *
+                          ((hp.g_dtype == MUON_BF16 ? 2 : 4) + (hp.m_dtype == MUON_BF16 ? 2 : 4));
+  mp.keep_gm = gm_bytes <= 128.0 * 1024 * 1024;
   mp.xscale = xs;
   mp.s = s;
   mp.partials = reinterpret_cast<float*>(env.ws + g.off_partials);

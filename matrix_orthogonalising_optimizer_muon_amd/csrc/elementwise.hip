@@ -117,7 +117,10 @@ __global__ __launch_bounds__(kNormThreads) void momentum_norm_kernel(const Momen
   const bool vec = (reinterpret_cast<uintptr_t>(d.G) % 16) == 0 && (reinterpret_cast<uintptr_t>(d.M) % 16) == 0 &&
                    e0 + 8 <= numel;
   float g[8], m[8];
-  if (vec) {
+  if (vec && p.keep_gm) {
+    load8<false>(d.G, e0, p.g_bf16, g);
+    load8<false>(d.M, e0, p.m_bf16, m);
+  } else if (vec) {
     load8<true>(d.G, e0, p.g_bf16, g);
     load8<true>(d.M, e0, p.m_bf16, m);
   } else {

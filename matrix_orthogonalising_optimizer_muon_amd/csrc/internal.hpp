@@ -146,6 +146,8 @@ struct MomentumParams {
   int32_t nesterov;
   int32_t g_bf16, m_bf16;   // storage dtypes (0: fp32)
   int32_t x_f16;            // iterate fp16 (bf16 path) or fp32
+  int32_t keep_gm;          // momentum_norm: ordinary (cached) loads of G and M, so that
+                            // momentum_x finds them in the caches (groups that fit)
   float xscale;             // power-of-two scale of the stored iterate
   const float* s;           // per-matrix 1 / (||U||_F + eps) (momentum_x)
   float* partials;          // [count][norm_blocks]

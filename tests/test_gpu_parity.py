@@ -121,8 +121,13 @@ def test_bf16_auto_dispatch_multi_step(B, ctx):
 
 
 def test_bf16_weight_update_bf16_weights(B, ctx):
-    """bf16-stored W: W' = bf16(W*(1 - lr*wd) - lr*O). One bf16 rounding of W' (half an
-    ulp, 2^-9 relative) dominates; the O error adds at most a few % of the step."""
+    """bf16-stored W: W' = bf16(W*(1 - lr*wd) - lr*O). The kernel rounds its fp32 W' once,
+    so W' must be the oracle's W' rounded to bf16 except where the O error (about 3e-3 of
+    lr*O, mostly far below a bf16 ulp of W) moves the value across a rounding boundary.
+    Checked: every element within one ulp of bf16(oracle W') plus lr times the O bar (2e-2)
+    of the largest |O| (the O error decides alone for weights near zero, whose ulp is
+    tiny), and few elements off bf16(oracle W') at all (a CPU simulation with a 3e-3
+    relative O error puts 6% of them one ulp off, 1e-2 puts 14%)."""
     w = wl.custom("bf16w", [(128, 384)], structure="gaussian", wid=206)
     w = wl.Workload(**{**w.__dict__, "w_dtype": "bf16"})
     st = GpuState(w)
@@ -131,11 +136,13 @@ def test_bf16_weight_update_bf16_weights(B, ctx):
     run_step(ctx, st, hp)
     W0 = wl.weight_np(w, 0).astype(np.float64)
     G = wl.gradient_np(w, 0, 0).astype(np.float64)
-    W_ref, _, _ = om.muon_step(W0, G, np.zeros_like(W0), mode="gram")
+    W_ref, _, O_ref = om.muon_step(W0, G, np.zeros_like(W0), mode="gram")
     W_gpu = to_np(st.W[0])
-    step = np.abs(W_ref - W0).max()
-    assert np.all(np.abs(W_gpu - W_ref) <= 2.0 ** -9 * np.abs(W_ref) + 0.05 * step)
-    assert rel(W_gpu - W0, W_ref - W0) < 0.1
+    W_ref_b = torch.from_numpy(W_ref).to(torch.bfloat16).double().numpy()
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(W_ref_b), 2.0 ** -126))) - 7)
+    off = np.abs(W_gpu - W_ref_b)
+    assert np.all(off <= ulp + w.lr * 2e-2 * np.abs(O_ref).max()), np.max(off / ulp)
+    assert np.mean(off > 0) <= 0.15, np.mean(off > 0)
 
 
 def test_bf16_2560x9728_full_size(B, ctx):

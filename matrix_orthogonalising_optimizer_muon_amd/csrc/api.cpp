@@ -331,9 +331,15 @@ struct StageTimer {
              double bytes) {
     if (!c || !(c->flags & MUON_FLAG_PROFILE) || c->records.size() >= kMaxRecords) return;
     if (c->next_event == c->event_pool.size()) {
+      // Timing-only events: without the system-scope fence an event record does not write
+      // back and invalidate the caches, which otherwise adds about 2 us to every timed launch
+      // (2560 squares 27.7 -> 25.9 us event-timed, closer to the kernel trace).
       hipEvent_t a, b;
-      if (hipEventCreate(&a) != hipSuccess) return;
-      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return;
+      if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return;
+      }
       c->event_pool.emplace_back(a, b);
     }
     const auto ev = c->event_pool[c->next_event];

@@ -436,7 +436,8 @@ def main():
                                  "step_ms_p10_p50_p90": [round(x, 4) for x in ra["pct"]],
                                  "plan": ra["plans"],
                                  **{k: sa[k] for k in ("roofline", "gemm_tflops", "gemm_frac_of_peak",
-                                                       "momentum_gbs", "hbm_phase_gbs", "profiled_ms_per_step",
+                                                       "momentum_gbs", "momentum_frac_of_hbm", "hbm_phase_gbs",
+                                                       "hbm_phase_frac_of_hbm", "profiled_ms_per_step",
                                                        "stages")}}
     modes = [x for x in args.also_modes.split(",") if x and x != args.mode] if args.also_modes else []
     if modes:

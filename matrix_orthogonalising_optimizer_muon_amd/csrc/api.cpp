@@ -84,7 +84,9 @@ struct Group {
   size_t off_partials = 0, off_s = 0, off_x = 0, off_xt[2] = {0, 0}, off_sq[4] = {0, 0, 0, 0};
   int64_t stride_x = 0, stride_sq = 0;
   int mom_tiles_m = 0, mom_tiles_n = 0;
-  int norm_blocks = 0;         // 4096-element blocks of one stored matrix (norm partials)
+  int norm_blocks = 0;         // norm-pass blocks of one stored matrix (one partial each)
+  int norm_ub = 1;             // kNormBlock-element groups per norm-pass block (1 or 4)
+  bool gm_cached = false;      // G and M small enough to stay in the caches between passes
   bool single_wg = false;      // whole update per matrix in one workgroup (small shapes)
   bool has_tall = false;       // some member is stored transposed (rows > cols)
   double work = 0.0;
@@ -271,7 +273,17 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
     g.mom_tiles_m = static_cast<int>(g.Mp / 64);
     g.mom_tiles_n = static_cast<int>(g.Np / 64);
     g.off_partials = off;
-    g.norm_blocks = static_cast<int>((g.m * g.n + kNormBlock - 1) / kNormBlock);
+    // The second momentum pass reads G and M again. When a group's G and M fit well inside
+    // the 256 MB Infinity Cache, the first pass loads them normally so the second finds them
+    // there (2560 x 9728: second pass 50-51 -> 42 us, first pass +1 us); larger groups
+    // stream them past the caches (cached loads made their first pass 3% slower, the second
+    // no faster) and take four groups of 8 elements per thread in the first pass.
+    const double gm_bytes = static_cast<double>(cnt) * g.m * g.n *
+                            ((hp.g_dtype == MUON_BF16 ? 2 : 4) + (hp.m_dtype == MUON_BF16 ? 2 : 4));
+    g.gm_cached = gm_bytes <= 128.0 * 1024 * 1024;
+    g.norm_ub = g.gm_cached ? 1 : 4;
+    const int64_t nb_elems = static_cast<int64_t>(kNormBlock) * g.norm_ub;
+    g.norm_blocks = static_cast<int>((g.m * g.n + nb_elems - 1) / nb_elems);
     off = align_up(off + sizeof(float) * cnt * g.norm_blocks);
     g.off_s = off;
     off = align_up(off + sizeof(float) * cnt);
@@ -700,13 +712,8 @@ int run_group(const Group& g, const StepEnv& env, MatDesc* table, const MatDesc*
   mp.count = count;
   mp.mu = hp.momentum; mp.nesterov = hp.nesterov;
   mp.g_bf16 = hp.g_dtype == MUON_BF16; mp.m_bf16 = hp.m_dtype == MUON_BF16; mp.x_f16 = !f32;
-  // The second pass reads G and M again. When a group's G and M fit well inside the 256 MB
-  // Infinity Cache, the first pass loads them normally so the second finds them there
-  // (2560 x 9728: second pass 50-51 -> 42 us, first pass +1 us); larger groups stream them
-  // past the caches (cached loads made their first pass 3% slower, the second no faster).
-  const double gm_bytes = static_cast<double>(count) * g.m * g.n *
-                          ((hp.g_dtype == MUON_BF16 ? 2 : 4) + (hp.m_dtype == MUON_BF16 ? 2 : 4));
-  mp.keep_gm = gm_bytes <= 128.0 * 1024 * 1024;
+  mp.keep_gm = g.gm_cached;
+  mp.norm_ub = g.norm_ub;
   mp.xscale = xs;
   mp.s = s;
   mp.partials = reinterpret_cast<float*>(env.ws + g.off_partials);
@@ -1249,6 +1256,7 @@ int muon_debug_stage(muon_ctx* ctx, int stage, const muon_matrix* mat, const muo
     mp.Mp = static_cast<int32_t>(g.Mp); mp.Np = static_cast<int32_t>(g.Np);
     mp.tiles_m = g.mom_tiles_m; mp.tiles_n = g.mom_tiles_n;
     mp.norm_blocks = g.norm_blocks;
+    mp.norm_ub = 1;
     mp.count = 1;
     mp.mu = hp->momentum; mp.nesterov = hp->nesterov;
     mp.g_bf16 = hp->g_dtype == MUON_BF16; mp.m_bf16 = hp->m_dtype == MUON_BF16; mp.x_f16 = !f32;

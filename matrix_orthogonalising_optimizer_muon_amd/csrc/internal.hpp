@@ -140,7 +140,9 @@ struct MomentumParams {
   int32_t m, n;           // canonical dims m' <= n'
   int32_t Mp, Np;         // padded canonical dims
   int32_t tiles_m, tiles_n;  // 64 x 64 canonical tiles per matrix (momentum_x grid)
-  int32_t norm_blocks;    // 4096-element blocks of the stored matrix (momentum_norm grid)
+  int32_t norm_blocks;    // norm_ub * kNormBlock-element blocks of the stored matrix
+                          // (momentum_norm grid, one partial each)
+  int32_t norm_ub;        // 1 or 4: kNormBlock-element groups per momentum_norm workgroup
   int32_t count;
   float mu;
   int32_t nesterov;

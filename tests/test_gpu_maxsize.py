@@ -120,27 +120,26 @@ def test_block_structure_premise():
         assert not O_full[~mask].any() and not M_new[~mask].any()
 
 
-@pytest.mark.gpu
-@pytest.mark.timeout(600)
-def test_max_dimension_block_structured(B):
-    rng = np.random.default_rng(20240920)
+def run_block_case(B, specs, seed, label):
+    """One muon_step over block-structured matrices (canonical m' x n', stored wide or tall)
+    and the checks of the module docstring; returns the worst O error."""
+    rng = np.random.default_rng(seed)
     mats, ref, parts = [], [], []
-    for k, (nrows, tall) in enumerate(SPECS):
-        rows, cols = blocks(rng, nrows)
+    for k, (nrows, ncols, tall) in enumerate(specs):
+        rows, cols = blocks(rng, nrows, ncols)
         Gb, Mb = draw(rng, rows, cols)
         ref.append(oracle_blocks(Gb, Mb))
         parts.append((rows, cols))
-        shape = (COLS, nrows) if tall else (nrows, COLS)
+        shape = (ncols, nrows) if tall else (nrows, ncols)
         G = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
         M = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
-        for t in range(NBLK):
+        for t in range(len(rows)):
             place(G, tall, rows[t], cols[t], Gb[t].cuda())
             place(M, tall, rows[t], cols[t], Mb[t].cuda())
         gen = torch.Generator(device="cuda").manual_seed(7 + k)
         W = 0.02 * torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
         mats.append((W, G, M, tall))
-        print(f"[maxsize] matrix {k} ({'tall' if tall else 'wide'} {shape[0]}x{shape[1]}) placed",
-              flush=True)
+        print(f"[{label}] matrix {k} ({'tall' if tall else 'wide'} {shape[0]}x{shape[1]}) placed", flush=True)
     W0 = [W.clone() for W, _, _, _ in mats]
     torch.cuda.synchronize()
 
@@ -150,27 +149,25 @@ def test_max_dimension_block_structured(B):
                             mode="gram", segments=(2, 2, 1), w_dtype="f32", g_dtype="bf16",
                             m_dtype="bf16", ns_dtype="bf16")
         triples = [(W, G, M) for W, G, M, _ in mats]
-        for i in range(len(triples)):
-            entry = B.muon_plan_info(ctx, triples, hp, i)
-            assert entry.tile_sym in (0, 1, 2, 3) and entry.tile_apply in (0, 1, 2, 3), \
-                "a 4 GiB iterate must run on register-staged tiles"
+        entries = [B.muon_plan_info(ctx, triples, hp, i) for i in range(len(triples))]
         nbytes = B.muon_workspace_size(ctx, triples, hp)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-        print(f"[maxsize] muon_step over {len(triples)} matrices, workspace {nbytes / 2**30:.1f} GiB", flush=True)
+        print(f"[{label}] muon_step over {len(triples)} matrices, workspace {nbytes / 2**30:.1f} GiB", flush=True)
         B.check(B.muon_step(ctx, triples, hp, ws.data_ptr(), nbytes), "muon_step")
         torch.cuda.synchronize()
-        print("[maxsize] step done", flush=True)
+        print(f"[{label}] step done", flush=True)
         del ws
     finally:
         B.muon_destroy(ctx)
 
+    worst = 0.0
     for k, (W, G, M, tall) in enumerate(mats):
         Mn, O = ref[k]
         rows, cols = parts[k]
         D = W0[k] - W                      # lr * O on the blocks, exactly zero elsewhere
         num = den = 0.0
         worst_m = 0.0
-        for t in range(NBLK):
+        for t in range(len(rows)):
             o_gpu = take(D, tall, rows[t], cols[t]).double().cpu().numpy() / LR
             num += float(np.sum((o_gpu - O[t]) ** 2))
             den += float(np.sum(O[t] ** 2))
@@ -181,9 +178,32 @@ def test_max_dimension_block_structured(B):
         err = (num / den) ** 0.5
         off_w = float(D.abs().max())
         off_m = float(M.abs().max())
-        print(f"[maxsize] matrix {k}: O error {err:.3e}, M' error {worst_m:.3e}, "
+        print(f"[{label}] matrix {k}: O error {err:.3e}, M' error {worst_m:.3e}, "
               f"off-block max |W' - W| {off_w}, max |M'| {off_m}", flush=True)
         assert off_w == 0.0 and off_m == 0.0, (k, off_w, off_m)
         assert err <= 2e-2, (k, err)
         assert worst_m <= 2.0 ** -8, (k, worst_m)
+        worst = max(worst, err)
         del D
+    return entries, worst
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(600)
+def test_max_dimension_block_structured(B):
+    entries, _ = run_block_case(B, [(m, COLS, tall) for m, tall in SPECS], 20240920, "maxsize")
+    for e in entries:
+        assert e.tile_sym in (0, 1, 2, 3) and e.tile_apply in (0, 1, 2, 3), \
+            "a 4 GiB iterate must run on register-staged tiles"
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(600)
+def test_large_ragged_block_structured(B):
+    """3000 x 45001 stored wide and tall (one group of two): ragged in both dimensions, G and
+    M over 128 MB, so the norm pass takes four groups of 8 per thread and its last block is
+    partial (135,003,000 elements, not a multiple of 16384); the iterate (3008 x 45056 fp16)
+    is under 4 GiB, so the direct-load tiles run."""
+    entries, _ = run_block_case(B, [(3000, 45001, False), (3000, 45001, True)], 20240921, "ragged")
+    for e in entries:
+        assert e.tile_apply not in (0, 1, 2, 3)

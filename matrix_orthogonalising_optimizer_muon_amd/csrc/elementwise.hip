@@ -173,13 +173,18 @@ __device__ __forceinline__ void store_x8(void* X, int64_t off, int f16, const fl
   }
 }
 
-// Pass 2: one workgroup per canonical 64 x 64 tile of the padded iterate. The tile is read
-// in the STORED layout (coalesced along stored rows; both passes' loads issued before any
-// store), M' is stored back, and x = xscale * s * u goes out twice:
+// Pass 2: TPW canonical 64 x 64 tiles of the padded iterate per workgroup. A tile is read
+// in the STORED layout (coalesced along stored rows; the loads of all TPW tiles issued
+// before any store), M' is stored back, and x = xscale * s * u goes out twice:
 //   * in the stored layout straight from registers: for a matrix stored in canonical
 //     orientation that is X (row-major), for a tall one (stored as the transpose) X^T;
 //   * through an LDS tile, transposed, as the other layout.
-// Tiles over the padding write zeros, so both layouts are zero outside m' x n'.
+// Tiles over the padding write zeros, so both layouts are zero outside m' x n'. TPW = 2 for
+// the groups whose first pass streams (more loads in flight per thread: 7B list's 84-matrix
+// pass 11.8 -> 10.7 ms and 9.73 -> 9.60 ms on two boxes, decoder 2048 x 8192 group 2.49 ->
+// 2.38 ms, 2048^2 group 0.83 -> 0.73 ms); a past-the-end second tile (odd tile counts)
+// loads the last tile again and stores nothing.
+template <int TPW>
 __global__ __launch_bounds__(kThreads) void momentum_x_kernel(const MomentumParams p) {
   __shared__ float tile[kTile][kTile + 1];
   const int mat = blockIdx.y;
@@ -187,69 +192,84 @@ __global__ __launch_bounds__(kThreads) void momentum_x_kernel(const MomentumPara
   const int tid = threadIdx.x;
   const bool vec_ok = (d.cols % 8) == 0 && (reinterpret_cast<uintptr_t>(d.G) % 16) == 0 &&
                       (reinterpret_cast<uintptr_t>(d.M) % 16) == 0;
-  const int t = blockIdx.x;
-  const int ti = t / p.tiles_n, tj = t % p.tiles_n;
-  const int i0 = ti * kTile, j0 = tj * kTile;   // canonical tile origin
+  const int ntiles = p.tiles_m * p.tiles_n;
   const int cr = tid >> 3;          // local row within a pass
   const int cc = (tid & 7) * 8;     // local first column (8 consecutive)
   const float sc = p.xscale * p.s[mat];
-  // stored tile origin, and where the two layouts of the tile start
-  const int64_t srow0 = d.transposed ? j0 : i0, scol0 = d.transposed ? i0 : j0;
   void* direct = d.transposed ? p.XT : p.X;     // layout that follows the stored rows
   void* other = d.transposed ? p.X : p.XT;
   const int64_t ld_direct = d.transposed ? p.Mp : p.Np, ld_other = d.transposed ? p.Np : p.Mp;
   const int64_t base = static_cast<int64_t>(mat) * p.sX;
 
-  float g[2][8], m[2][8];
-  bool full[2];
+  float g[TPW][2][8], m[TPW][2][8];
+  bool full[TPW][2];
+  int64_t srow0[TPW], scol0[TPW];
+  bool valid[TPW];
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int64_t sr = srow0 + cr + pass * 32;
-    const int64_t sc0 = scol0 + cc;
-    full[pass] = vec_ok && sr < d.rows && sc0 + 8 <= d.cols;
-    if (full[pass]) {
-      load8<true>(d.G, sr * d.cols + sc0, p.g_bf16, g[pass]);
-      load8<true>(d.M, sr * d.cols + sc0, p.m_bf16, m[pass]);
-    } else {
+  for (int u = 0; u < TPW; ++u) {
+    const int t0 = blockIdx.x * TPW + u;
+    valid[u] = t0 < ntiles;
+    const int t = valid[u] ? t0 : ntiles - 1;
+    const int ti = t / p.tiles_n, tj = t % p.tiles_n;
+    const int i0 = ti * kTile, j0 = tj * kTile;
+    srow0[u] = d.transposed ? j0 : i0;
+    scol0[u] = d.transposed ? i0 : j0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool ok = sr < d.rows && sc0 + e < d.cols;
-        g[pass][e] = ok ? load_elem(d.G, sr * d.cols + sc0 + e, p.g_bf16) : 0.0f;
-        m[pass][e] = ok ? load_elem(d.M, sr * d.cols + sc0 + e, p.m_bf16) : 0.0f;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int64_t sr = srow0[u] + cr + pass * 32;
+      const int64_t sc0 = scol0[u] + cc;
+      full[u][pass] = vec_ok && sr < d.rows && sc0 + 8 <= d.cols;
+      if (full[u][pass]) {
+        load8<true>(d.G, sr * d.cols + sc0, p.g_bf16, g[u][pass]);
+        load8<true>(d.M, sr * d.cols + sc0, p.m_bf16, m[u][pass]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool ok = sr < d.rows && sc0 + e < d.cols;
+          g[u][pass][e] = ok ? load_elem(d.G, sr * d.cols + sc0 + e, p.g_bf16) : 0.0f;
+          m[u][pass][e] = ok ? load_elem(d.M, sr * d.cols + sc0 + e, p.m_bf16) : 0.0f;
+        }
       }
     }
   }
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int lr = cr + pass * 32;
-    const int64_t sr = srow0 + lr;
-    const int64_t sc0 = scol0 + cc;
-    const Mom8 r = momentum8(p, g[pass], m[pass]);
-    if (full[pass]) {
-      store8<true>(d.M, sr * d.cols + sc0, p.m_bf16, r.mn);
-    } else {
+  for (int u = 0; u < TPW; ++u) {
+    if (u > 0) __syncthreads();   // the previous tile's LDS reads are done
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (sr < d.rows && sc0 + e < d.cols) store_elem(d.M, sr * d.cols + sc0 + e, r.mn[e], p.m_bf16);
+    for (int pass = 0; pass < 2; ++pass) {
+      const int lr = cr + pass * 32;
+      const int64_t sr = srow0[u] + lr;
+      const int64_t sc0 = scol0[u] + cc;
+      const Mom8 r = momentum8(p, g[u][pass], m[u][pass]);
+      if (valid[u]) {
+        if (full[u][pass]) {
+          store8<true>(d.M, sr * d.cols + sc0, p.m_bf16, r.mn);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (sr < d.rows && sc0 + e < d.cols) store_elem(d.M, sr * d.cols + sc0 + e, r.mn[e], p.m_bf16);
+        }
+      }
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = sc * r.u[e];
+        tile[lr][cc + e] = x[e];
+      }
+      if (valid[u]) store_x8(direct, base + (srow0[u] + lr) * ld_direct + scol0[u] + cc, p.x_f16, x);
     }
-    float x[8];
+    __syncthreads();
+    if (valid[u]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // the padding (out of the stored matrix) is zero: g = m = 0 gave u = 0 there
-      x[e] = sc * r.u[e];
-      tile[lr][cc + e] = x[e];
+      for (int pass = 0; pass < 2; ++pass) {
+        const int lr = cr + pass * 32;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = tile[cc + e][lr];
+        const int64_t off = (scol0[u] + lr) * ld_other + srow0[u] + cc;
+        store_x8(other, base + off, p.x_f16, v);
+      }
     }
-    store_x8(direct, base + (srow0 + lr) * ld_direct + scol0 + cc, p.x_f16, x);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int lr = cr + pass * 32;   // column of the LDS tile = row of the other layout
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = tile[cc + e][lr];
-    const int64_t off = (scol0 + lr) * ld_other + srow0 + cc;
-    store_x8(other, base + off, p.x_f16, v);
   }
 }
 
@@ -336,7 +356,11 @@ hipError_t launch_momentum_norm(const MomentumParams& p, hipStream_t st) {
 
 hipError_t launch_momentum_x(const MomentumParams& p, hipStream_t st) {
   if (p.count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(momentum_x_kernel, dim3(p.tiles_m * p.tiles_n, p.count), dim3(kThreads), 0, st, p);
+  const int nt = p.tiles_m * p.tiles_n;
+  if (p.norm_ub == 4)   // the large groups (G and M past the caches)
+    hipLaunchKernelGGL(momentum_x_kernel<2>, dim3((nt + 1) / 2, p.count), dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(momentum_x_kernel<1>, dim3(nt, p.count), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -143,6 +143,7 @@ struct MomentumParams {
   int32_t norm_blocks;    // norm_ub * kNormBlock-element blocks of the stored matrix
                           // (momentum_norm grid, one partial each)
   int32_t norm_ub;        // 1 or 4: kNormBlock-element groups per momentum_norm workgroup
+                          // (4: a large group, whose momentum_x workgroups take two tiles)
   int32_t count;
   float mu;
   int32_t nesterov;

@@ -200,10 +200,11 @@ def test_max_dimension_block_structured(B):
 @pytest.mark.gpu
 @pytest.mark.timeout(600)
 def test_large_ragged_block_structured(B):
-    """3000 x 45001 stored wide and tall (one group of two): ragged in both dimensions, G and
-    M over 128 MB, so the norm pass takes four groups of 8 per thread and its last block is
-    partial (135,003,000 elements, not a multiple of 16384); the iterate (3008 x 45056 fp16)
-    is under 4 GiB, so the direct-load tiles run."""
-    entries, _ = run_block_case(B, [(3000, 45001, False), (3000, 45001, True)], 20240921, "ragged")
+    """3000 x 44990 stored wide and tall (one group of two): ragged in both dimensions, G and
+    M over 128 MB, so the momentum passes take their large-group forms: the norm pass's last
+    block is partial (134,970,000 elements, not a multiple of 16384) and the 64 x 64 tiles
+    of the iterate pass are odd in number (47 x 703). The iterate (3008 x 44992 fp16) is under
+    4 GiB, so the direct-load tiles run."""
+    entries, _ = run_block_case(B, [(3000, 44990, False), (3000, 44990, True)], 20240921, "ragged")
     for e in entries:
         assert e.tile_apply not in (0, 1, 2, 3)

@@ -355,3 +355,17 @@ def test_error_leaves_state_untouched(B, ctx):
     assert B.muon_step(ctx, mats, bad, ws.data_ptr(), nbytes) == B.MUON_ERR_ARG
     torch.cuda.synchronize()
     assert torch.equal(st.W[0], W0) and torch.equal(st.M[0], M0)
+
+
+def test_empty_list_is_a_noop(B, ctx):
+    """count == 0 on a device context: MUON_OK, no workspace needed, nothing launched (a
+    matrix the call does not name stays as it was)."""
+    w = wl.custom("empty", [(64, 256)], structure="gaussian", wid=210)
+    st = GpuState(w)
+    st.load_gradients(0)
+    W0, M0 = st.W[0].clone(), st.M[0].clone()
+    arr = B.matrix_list(st.triples(), B.make_hparams())
+    assert B.muon_workspace_size(ctx, [], B.make_hparams()) == 0
+    assert B.muon_step(ctx, arr, B.make_hparams(), 0, 0, count=0) == B.MUON_OK
+    torch.cuda.synchronize()
+    assert torch.equal(st.W[0], W0) and torch.equal(st.M[0], M0)

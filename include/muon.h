@@ -295,8 +295,10 @@ int muon_debug_gemm(muon_ctx *ctx, int kind, int ns_dtype, int tile, int64_t M, 
  *                       the iterate's type; O's canonical m' x n' block goes to W through the
  *                       orientation map (transposed for rows > cols); out must be non-null
  *                       (unused). G and M may be null.
- * *scale (host, may be null) receives the iterate's scale. The workspace needs 512 bytes
- * plus 4 per 4096 elements of the matrix (rounded up to 256), 256-byte aligned. Validation
+ * The stages run the kernel forms muon_step runs for this matrix alone (G and M over
+ * 128 MB take the large-group forms). *scale (host, may be null) receives the iterate's
+ * scale. The workspace needs 512 bytes plus 4 per 4096 elements of the matrix (rounded up
+ * to 256), 256-byte aligned. Validation
  * as muon_step (MUON_ERR_ARG also for a null operand the stage uses). */
 #define MUON_STAGE_NORM 0
 #define MUON_STAGE_ITERATE 1

@@ -211,6 +211,21 @@ void choose_schedule(const muon_ctx* ctx, Group& g, const muon_hparams& hp, bool
 // list uses the kernel only when every group qualifies.
 bool single_wg_shape(int64_t Mp, int64_t Np) { return Mp <= 128 && Mp * Np <= kSmallMaxElems; }
 
+// The second momentum pass reads G and M again. When a group's G and M fit well inside the
+// 256 MB Infinity Cache, the first pass loads them normally so the second finds them there
+// (2560 x 9728: second pass 50-51 -> 42 us, first pass +1 us). Larger groups stream them past
+// the caches (cached loads made their first pass 3% slower, the second no faster) and put
+// more loads in flight per thread: four groups of 8 elements per thread in the first pass,
+// two tiles per workgroup in the second.
+void set_norm_blocking(Group& g, const muon_hparams& hp, size_t cnt) {
+  const double gm_bytes = static_cast<double>(cnt) * g.m * g.n *
+                          ((hp.g_dtype == MUON_BF16 ? 2 : 4) + (hp.m_dtype == MUON_BF16 ? 2 : 4));
+  g.gm_cached = gm_bytes <= 128.0 * 1024 * 1024;
+  g.norm_ub = g.gm_cached ? 1 : 4;
+  const int64_t nb_elems = static_cast<int64_t>(kNormBlock) * g.norm_ub;
+  g.norm_blocks = static_cast<int>((g.m * g.n + nb_elems - 1) / nb_elems);
+}
+
 int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const muon_hparams& hp,
                bool need_ptrs, Plan& plan) {
   plan = Plan{};
@@ -273,17 +288,7 @@ int build_plan(const muon_ctx* ctx, const muon_matrix* mats, int count, const mu
     g.mom_tiles_m = static_cast<int>(g.Mp / 64);
     g.mom_tiles_n = static_cast<int>(g.Np / 64);
     g.off_partials = off;
-    // The second momentum pass reads G and M again. When a group's G and M fit well inside
-    // the 256 MB Infinity Cache, the first pass loads them normally so the second finds them
-    // there (2560 x 9728: second pass 50-51 -> 42 us, first pass +1 us); larger groups
-    // stream them past the caches (cached loads made their first pass 3% slower, the second
-    // no faster) and take four groups of 8 elements per thread in the first pass.
-    const double gm_bytes = static_cast<double>(cnt) * g.m * g.n *
-                            ((hp.g_dtype == MUON_BF16 ? 2 : 4) + (hp.m_dtype == MUON_BF16 ? 2 : 4));
-    g.gm_cached = gm_bytes <= 128.0 * 1024 * 1024;
-    g.norm_ub = g.gm_cached ? 1 : 4;
-    const int64_t nb_elems = static_cast<int64_t>(kNormBlock) * g.norm_ub;
-    g.norm_blocks = static_cast<int>((g.m * g.n + nb_elems - 1) / nb_elems);
+    set_norm_blocking(g, hp, cnt);
     off = align_up(off + sizeof(float) * cnt * g.norm_blocks);
     g.off_s = off;
     off = align_up(off + sizeof(float) * cnt);
@@ -1215,7 +1220,7 @@ int muon_debug_stage(muon_ctx* ctx, int stage, const muon_matrix* mat, const muo
     g.members = {0};
     g.has_tall = mat->rows > mat->cols;
     g.mom_tiles_m = static_cast<int>(g.Mp / 64); g.mom_tiles_n = static_cast<int>(g.Np / 64);
-    g.norm_blocks = static_cast<int>((g.m * g.n + kNormBlock - 1) / kNormBlock);
+    set_norm_blocking(g, *hp, 1);   // the kernels muon_step runs for this matrix alone
     g.stride_x = g.Mp * g.Np; g.stride_sq = g.Mp * g.Mp;
     const bool f32 = hp->ns_dtype == MUON_F32;
     g.tile_ap = heuristic_apply(g.Mp, g.Np, 1, ctx->cu_count, f32);
@@ -1256,7 +1261,8 @@ int muon_debug_stage(muon_ctx* ctx, int stage, const muon_matrix* mat, const muo
     mp.Mp = static_cast<int32_t>(g.Mp); mp.Np = static_cast<int32_t>(g.Np);
     mp.tiles_m = g.mom_tiles_m; mp.tiles_n = g.mom_tiles_n;
     mp.norm_blocks = g.norm_blocks;
-    mp.norm_ub = 1;
+    mp.norm_ub = g.norm_ub;
+    mp.keep_gm = g.gm_cached;
     mp.count = 1;
     mp.mu = hp->momentum; mp.nesterov = hp->nesterov;
     mp.g_bf16 = hp->g_dtype == MUON_BF16; mp.m_bf16 = hp->m_dtype == MUON_BF16; mp.x_f16 = !f32;

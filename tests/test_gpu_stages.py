@@ -53,6 +53,19 @@ def workspace(rows, cols):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_norm_and_iterate(B, ctx, shape, dtype, nesterov):
+    check_norm_and_iterate(B, ctx, shape, dtype, nesterov)
+
+
+@pytest.mark.parametrize("shape", [(9000, 4001), (4001, 9000)])
+def test_norm_and_iterate_large(B, ctx, shape):
+    """G and M over 128 MB (36,009,000 bf16 elements each): the forms muon_step runs for
+    large groups, four groups of 8 per thread in the norm pass (a partial last block:
+    36,009,000 is not a multiple of 16384) and two 64 x 64 tiles per workgroup in the
+    iterate pass (63 x 141 tiles, an odd count)."""
+    check_norm_and_iterate(B, ctx, shape, "bf16", True)
+
+
+def check_norm_and_iterate(B, ctx, shape, dtype, nesterov):
     rows, cols = shape
     G, M, _ = inputs(rows, cols, dtype, seed=rows * 7 + cols)
     hp = B.make_hparams(g_dtype=dtype, m_dtype=dtype, ns_dtype=dtype, nesterov=nesterov, momentum=0.9, eps=1e-7)

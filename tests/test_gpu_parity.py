@@ -81,7 +81,8 @@ def check_step(B, ctx, w, indices=None, mode="gram", segments=(2, 2, 1), steps=1
 
 @pytest.mark.parametrize("mode", ["plain", "gram"])
 def test_fp32_single_256x1024(B, ctx, mode):
-    check_step(B, ctx, wl.WORKLOADS["single_fp32_256x1024"], mode=mode)
+    e = check_step(B, ctx, wl.WORKLOADS["single_fp32_256x1024"], mode=mode)
+    print(f"[parity] fp32 256x1024 {mode}: O error {e:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("mode,segments", [("gram", (2, 3)), ("gram", (1, 1, 1, 1, 1)), ("gram", (5,)),
@@ -150,6 +151,7 @@ def test_bf16_2560x9728_full_size(B, ctx):
     w = wl.WORKLOADS["single_bf16_2560x9728"]
     e_gram = check_step(B, ctx, w, mode="gram")
     e_plain = check_step(B, ctx, w, mode="plain")
+    print(f"[parity] 2560x9728: O error Gram 2+2+1 {e_gram:.3e}, plain {e_plain:.3e}", flush=True)
     assert e_gram <= 2e-2 and e_plain <= 2e-2
 
 
@@ -244,7 +246,8 @@ def test_concurrent_groups(B, ctx):
 
 def test_small_batch_832_full(B, ctx):
     w = wl.WORKLOADS["small_batch_832"]
-    check_step(B, ctx, w, mode="gram", gpu_mode="auto")
+    e = check_step(B, ctx, w, mode="gram", gpu_mode="auto")
+    print(f"[parity] 832 matrices: worst O error {e:.3e}", flush=True)
 
 
 @pytest.fixture(scope="module")
